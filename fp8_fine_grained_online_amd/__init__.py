@@ -1,0 +1,35 @@
+"""fp8_fine_grained_online_amd: fine-grained online FP8 quantization and the
+block-scaled FP8 GEMM on AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libfp8q.so`` (C ABI, ``include/fp8q.h``).
+This module only marshals arguments: it checks tensor dtypes/devices/layouts,
+allocates outputs with torch when the caller does not pass them, and forwards
+raw device pointers and torch's current HIP stream. There is no other path:
+if the library is missing, every call raises.
+
+Entry points (same names as the C ABI):
+  fp8q_quant_act_1x128(x)                    -> (q, sa)
+  fp8q_quant_weight_128x128(w)               -> (q, sb)
+  fp8_gemm_blockscaled(a, sa, b, sb, out_dtype)          -> c
+  fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype)   -> c
+"""
+
+from ._lib import (  # noqa: F401
+    Fp8qError,
+    FP8Q_OUT_BF16,
+    FP8Q_OUT_F32,
+    STATUS,
+    fp8_gemm_blockscaled,
+    fp8_gemm_grouped,
+    fp8q_quant_act_1x128,
+    fp8q_quant_weight_128x128,
+    fp8q_version,
+    lib,
+    lib_path,
+)
+
+__all__ = [
+    "Fp8qError", "FP8Q_OUT_BF16", "FP8Q_OUT_F32", "STATUS",
+    "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
+    "fp8_gemm_blockscaled", "fp8_gemm_grouped", "fp8q_version", "lib", "lib_path",
+]

@@ -1,0 +1,191 @@
+"""ctypes binding of libfp8q.so: argument marshalling only."""
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG_DIR, "libfp8q.so")
+
+FP8Q_OUT_F32 = 0
+FP8Q_OUT_BF16 = 1
+
+STATUS = {
+    0: "FP8Q_OK", 1: "FP8Q_ERR_NULL", 2: "FP8Q_ERR_SHAPE", 3: "FP8Q_ERR_ALIGN",
+    4: "FP8Q_ERR_DTYPE", 5: "FP8Q_ERR_LAUNCH", 6: "FP8Q_ERR_NO_DEVICE", 7: "FP8Q_ERR_TOO_LARGE",
+}
+
+_lib = None
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"{_LIB_PATH} is missing: build it with `python -m fp8_fine_grained_online_amd.build`"
+                " (there is no fallback path)")
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.fp8q_version.restype = i32
+        L.fp8q_version.argtypes = []
+        L.fp8q_status_string.restype = ctypes.c_char_p
+        L.fp8q_status_string.argtypes = [i32]
+        L.fp8q_quant_act_1x128.restype = i32
+        L.fp8q_quant_act_1x128.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fp8q_quant_weight_128x128.restype = i32
+        L.fp8q_quant_weight_128x128.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fp8_gemm_blockscaled.restype = i32
+        L.fp8_gemm_blockscaled.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+        L.fp8_gemm_grouped.restype = i32
+        L.fp8_gemm_grouped.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, vp]
+        _lib = L
+    return _lib
+
+
+def fp8q_version() -> int:
+    return lib().fp8q_version()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Fp8qError(fn, status, lib().fp8q_status_string(status).decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _out(t, name, shape, dtype, device):
+    torch = _torch()
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def fp8q_quant_act_1x128(x, q=None, sa=None, stream=None):
+    """x: bf16 M x K device tensor -> (q uint8 M x K, sa float32 M x K/128)."""
+    torch = _torch()
+    px = _dev(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    q = _out(q, "q", (M, K), torch.uint8, x.device)
+    sa = _out(sa, "sa", (M, K // 128 if K % 128 == 0 else 0), torch.float32, x.device)
+    _check("fp8q_quant_act_1x128",
+           lib().fp8q_quant_act_1x128(px, M, K, q.data_ptr(), sa.data_ptr(), _stream(stream)))
+    return q, sa
+
+
+def fp8q_quant_weight_128x128(w, q=None, sb=None, stream=None):
+    """w: bf16 N x K (or G x N x K) device tensor -> (q uint8 like w, sb float32 .../128 x K/128)."""
+    torch = _torch()
+    if w.dim() == 3:
+        G, N, K = w.shape
+        q = _out(q, "q", (G, N, K), torch.uint8, w.device)
+        sb = _out(sb, "sb", (G, N // 128, K // 128), torch.float32, w.device)
+        _dev(w, "w", torch.bfloat16, 3)
+        rows = G * N
+    else:
+        _dev(w, "w", torch.bfloat16, 2)
+        N, K = w.shape
+        q = _out(q, "q", (N, K), torch.uint8, w.device)
+        sb = _out(sb, "sb", (N // 128, K // 128), torch.float32, w.device)
+        rows = N
+    if w.dim() == 3 and N % 128:
+        raise ValueError("per-expert N must be a multiple of 128")
+    _check("fp8q_quant_weight_128x128",
+           lib().fp8q_quant_weight_128x128(w.data_ptr(), rows, K, q.data_ptr(), sb.data_ptr(),
+                                           _stream(stream)))
+    return q, sb
+
+
+def _out_dtype(out_dtype):
+    torch = _torch()
+    if out_dtype in (torch.bfloat16, "bf16", FP8Q_OUT_BF16):
+        return FP8Q_OUT_BF16, torch.bfloat16
+    if out_dtype in (torch.float32, "f32", FP8Q_OUT_F32):
+        return FP8Q_OUT_F32, torch.float32
+    raise ValueError(f"unsupported out_dtype {out_dtype}")
+
+
+def fp8_gemm_blockscaled(a, sa, b, sb, out_dtype="bf16", c=None, stream=None):
+    """C = A * B^T with per-1x128 (sa) and per-128x128 (sb) scales. Returns c (M x N)."""
+    torch = _torch()
+    code, tdt = _out_dtype(out_dtype)
+    pa = _dev(a, "a", torch.uint8, 2)
+    psa = _dev(sa, "sa", torch.float32, 2)
+    pb = _dev(b, "b", torch.uint8, 2)
+    psb = _dev(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if K % 128 == 0 and N % 128 == 0:
+        if tuple(sa.shape) != (M, K // 128) or tuple(sb.shape) != (N // 128, K // 128):
+            raise ValueError("scale shapes must be (M, K/128) and (N/128, K/128)")
+    c = _out(c, "c", (M, N), tdt, a.device)
+    _check("fp8_gemm_blockscaled",
+           lib().fp8_gemm_blockscaled(pa, psa, pb, psb, c.data_ptr(), code, M, N, K,
+                                      _stream(stream)))
+    return c
+
+
+def fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype="bf16", c=None, M_total=None, stream=None):
+    """Grouped GEMM. b: G x N x K codes, sb: G x N/128 x K/128, m_offsets: int32[G+1] device.
+
+    M_total defaults to a.shape[0] (the host-side row count; m_offsets is never
+    read on the host).
+    """
+    torch = _torch()
+    code, tdt = _out_dtype(out_dtype)
+    pa = _dev(a, "a", torch.uint8, 2)
+    psa = _dev(sa, "sa", torch.float32, 2)
+    pb = _dev(b, "b", torch.uint8, 3)
+    psb = _dev(sb, "sb", torch.float32, 3)
+    poff = _dev(m_offsets, "m_offsets", torch.int32, 1)
+    G, N, K = b.shape
+    if m_offsets.shape[0] != G + 1:
+        raise ValueError("m_offsets must have G+1 entries")
+    M = a.shape[0] if M_total is None else int(M_total)
+    if a.shape[1] != K or a.shape[0] < M:
+        raise ValueError("a must be at least M_total x K")
+    c = _out(c, "c", (M, N), tdt, a.device)
+    _check("fp8_gemm_grouped",
+           lib().fp8_gemm_grouped(pa, psa, pb, psb, c.data_ptr(), code, poff, G, M, N, K,
+                                  _stream(stream)))
+    return c

@@ -1,0 +1,137 @@
+// C ABI of the fp8q library: host-side argument checks, then kernel launches.
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state and can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/fp8q.h"
+
+namespace fp8q {
+hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
+                                  hipStream_t stream);
+hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* q, float* sb,
+                                       hipStream_t stream);
+hipError_t launch_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                   const float* sb, void* c, bool bf16_out, int64_t M, int64_t N,
+                                   int64_t K, hipStream_t stream);
+hipError_t launch_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b,
+                               const float* sb, void* c, bool bf16_out, const int32_t* m_offsets,
+                               int64_t G, int64_t M_total, int64_t N, int64_t K,
+                               hipStream_t stream);
+}  // namespace fp8q
+
+namespace {
+
+constexpr int64_t kGroup = 128;
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;  // kernels index rows/cols with int32
+constexpr int kMaxDevices = 64;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// 0 = unknown, 1 = gfx950, 2 = other; one slot per device ordinal.
+std::atomic<int> g_device_kind[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8Q_ERR_NO_DEVICE;
+  if (dev >= kMaxDevices) return FP8Q_ERR_NO_DEVICE;
+  int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8Q_ERR_NO_DEVICE;
+    kind = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_kind[dev].store(kind, std::memory_order_relaxed);
+  }
+  return kind == 1 ? FP8Q_OK : FP8Q_ERR_NO_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
+
+int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                      const void* c, int out_dtype, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
+  if (N % kGroup || K % kGroup) return FP8Q_ERR_SHAPE;
+  if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_TOO_LARGE;
+  if ((M + 127) / 128 * (N / 128) > kMaxDim) return FP8Q_ERR_TOO_LARGE;
+  if (M == 0 || N == 0) return -1;  // valid no-op
+  if (!c) return FP8Q_ERR_NULL;
+  if (K > 0 && (!a || !sa || !b || !sb)) return FP8Q_ERR_NULL;  // K == 0 reads no operand
+  if (!aligned(c, 16)) return FP8Q_ERR_ALIGN;
+  if (K > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4)))
+    return FP8Q_ERR_ALIGN;
+  return FP8Q_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8q_version(void) { return 100; }
+
+const char* fp8q_status_string(int status) {
+  switch (status) {
+    case FP8Q_OK: return "ok";
+    case FP8Q_ERR_NULL: return "a required pointer is NULL";
+    case FP8Q_ERR_SHAPE: return "invalid shape (negative size, K or N not a multiple of 128, or G < 1)";
+    case FP8Q_ERR_ALIGN: return "misaligned pointer (16 bytes for data, 4 bytes for scales)";
+    case FP8Q_ERR_DTYPE: return "unknown output dtype";
+    case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+    case FP8Q_ERR_NO_DEVICE: return "no gfx950 device is current";
+    case FP8Q_ERR_TOO_LARGE: return "size exceeds the kernels' 32-bit indexing";
+    default: return "unknown status";
+  }
+}
+
+int fp8q_quant_act_1x128(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,
+                         void* stream) {
+  if (M < 0 || K < 0 || K % kGroup) return FP8Q_ERR_SHAPE;
+  if (M > kMaxDim || K > kMaxDim || M * (K / kGroup) > (kMaxDim / 16)) return FP8Q_ERR_TOO_LARGE;
+  if (M == 0 || K == 0) return FP8Q_OK;
+  if (!x_bf16 || !q || !sa) return FP8Q_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(sa, 4)) return FP8Q_ERR_ALIGN;
+  if (int s = check_device()) return s;
+  return launched(fp8q::launch_quant_act_1x128(x_bf16, M, K, q, sa, (hipStream_t)stream));
+}
+
+int fp8q_quant_weight_128x128(const void* w_bf16, int64_t N, int64_t K, uint8_t* q, float* sb,
+                              void* stream) {
+  if (N < 0 || K < 0 || N % kGroup || K % kGroup) return FP8Q_ERR_SHAPE;
+  if (N / kGroup > 65535 || K > kMaxDim) return FP8Q_ERR_TOO_LARGE;
+  if (N == 0 || K == 0) return FP8Q_OK;
+  if (!w_bf16 || !q || !sb) return FP8Q_ERR_NULL;
+  if (!aligned(w_bf16, 16) || !aligned(q, 16) || !aligned(sb, 4)) return FP8Q_ERR_ALIGN;
+  if (int s = check_device()) return s;
+  return launched(fp8q::launch_quant_weight_128x128(w_bf16, N, K, q, sb, (hipStream_t)stream));
+}
+
+int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                         void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  int s = check_gemm_common(a, sa, b, sb, c, out_dtype, M, N, K);
+  if (s == -1) return FP8Q_OK;
+  if (s) return s;
+  if ((s = check_device())) return s;
+  return launched(fp8q::launch_gemm_blockscaled(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16, M, N,
+                                                K, (hipStream_t)stream));
+}
+
+int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                     void* c, int out_dtype, const int32_t* m_offsets, int64_t G, int64_t M_total,
+                     int64_t N, int64_t K, void* stream) {
+  if (G < 1) return FP8Q_ERR_SHAPE;
+  if (M_total % kGroup) return FP8Q_ERR_SHAPE;
+  if (G > kMaxDim || G * N > kMaxDim) return FP8Q_ERR_TOO_LARGE;
+  int s = check_gemm_common(a, sa, b, sb, c, out_dtype, M_total, N, K);
+  if (s == -1) return FP8Q_OK;
+  if (s) return s;
+  if (!m_offsets) return FP8Q_ERR_NULL;
+  if (!aligned(m_offsets, 4)) return FP8Q_ERR_ALIGN;
+  if ((s = check_device())) return s;
+  return launched(fp8q::launch_gemm_grouped(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16,
+                                            m_offsets, G, M_total, N, K, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+entry point, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+def _lib():
+    from fp8_fine_grained_online_amd import _lib as L
+    if not os.path.exists(L.lib_path()):
+        pytest.fail("libfp8q.so not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"FP8Q_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_four_entry_points():
+    syms = declared_symbols()
+    for name in ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
+                 "fp8_gemm_grouped", "fp8q_version", "fp8q_status_string"]:
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert L.fp8q_version() == 100
+    for s in range(8):
+        assert L.fp8q_status_string(s)
+    assert L.fp8q_status_string(99) == b"unknown status"
+
+
+# fake, suitably aligned addresses: never dereferenced, validation fails first
+P = 0x100000
+A, SA, B, SB, C, OFF, X, Q = (P * i for i in range(1, 9))
+
+
+def test_quant_act_validation():
+    L = _lib()
+    f = L.fp8q_quant_act_1x128
+    assert f(X, 4, 100, Q, SA, None) == 2  # K % 128
+    assert f(X, -1, 128, Q, SA, None) == 2
+    assert f(X, 4, -128, Q, SA, None) == 2
+    assert f(None, 4, 128, Q, SA, None) == 1
+    assert f(X, 4, 128, None, SA, None) == 1
+    assert f(X, 4, 128, Q, None, None) == 1
+    assert f(X + 2, 4, 128, Q, SA, None) == 3
+    assert f(X, 4, 128, Q + 8, SA, None) == 3
+    assert f(X, 4, 128, Q, SA + 2, None) == 3
+    assert f(X, 1 << 31, 128, Q, SA, None) == 7
+    # zero sizes: success without touching anything (NULL pointers allowed)
+    assert f(None, 0, 128, None, None, None) == 0
+    assert f(None, 5, 0, None, None, None) == 0
+
+
+def test_quant_weight_validation():
+    L = _lib()
+    f = L.fp8q_quant_weight_128x128
+    assert f(X, 100, 128, Q, SB, None) == 2
+    assert f(X, 128, 100, Q, SB, None) == 2
+    assert f(X, -128, 128, Q, SB, None) == 2
+    assert f(None, 128, 128, Q, SB, None) == 1
+    assert f(X, 128, 128, Q, None, None) == 1
+    assert f(X + 4, 128, 128, Q, SB, None) == 3
+    assert f(X, 128, 128, Q, SB + 1, None) == 3
+    assert f(X, 128 * 65536, 128, Q, SB, None) == 7
+    assert f(None, 0, 128, None, None, None) == 0
+
+
+def test_gemm_validation():
+    L = _lib()
+    f = L.fp8_gemm_blockscaled
+    assert f(A, SA, B, SB, C, 1, 64, 100, 128, None) == 2  # N % 128
+    assert f(A, SA, B, SB, C, 1, 64, 128, 100, None) == 2  # K % 128
+    assert f(A, SA, B, SB, C, 1, -1, 128, 128, None) == 2
+    assert f(A, SA, B, SB, C, 2, 64, 128, 128, None) == 4  # dtype
+    assert f(A, SA, B, SB, C, -1, 64, 128, 128, None) == 4
+    for i in range(5):
+        args = [A, SA, B, SB, C]
+        args[i] = None
+        assert f(*args, 1, 64, 128, 128, None) == 1, i
+    assert f(A + 8, SA, B, SB, C, 1, 64, 128, 128, None) == 3
+    assert f(A, SA, B + 1, SB, C, 1, 64, 128, 128, None) == 3
+    assert f(A, SA, B, SB, C + 4, 0, 64, 128, 128, None) == 3
+    assert f(A, SA + 2, B, SB, C, 0, 64, 128, 128, None) == 3
+    assert f(A, SA, B, SB + 2, C, 0, 64, 128, 128, None) == 3
+    assert f(A, SA, B, SB, C, 0, 1 << 31, 128, 128, None) == 7
+    assert f(None, None, None, None, None, 0, 0, 128, 128, None) == 0
+    assert f(None, None, None, None, None, 0, 64, 0, 128, None) == 0
+
+
+def test_grouped_validation():
+    L = _lib()
+    f = L.fp8_gemm_grouped
+    assert f(A, SA, B, SB, C, 1, OFF, 0, 256, 128, 128, None) == 2  # G < 1
+    assert f(A, SA, B, SB, C, 1, OFF, 2, 200, 128, 128, None) == 2  # M_total % 128
+    assert f(A, SA, B, SB, C, 1, OFF, 2, 256, 100, 128, None) == 2
+    assert f(A, SA, B, SB, C, 1, OFF, 2, 256, 128, 100, None) == 2
+    assert f(A, SA, B, SB, C, 3, OFF, 2, 256, 128, 128, None) == 4
+    assert f(A, SA, B, SB, C, 1, None, 2, 256, 128, 128, None) == 1
+    assert f(A, SA, B, SB, C, 1, OFF + 2, 2, 256, 128, 128, None) == 3
+    assert f(None, SA, B, SB, C, 1, OFF, 2, 256, 128, 128, None) == 1
+    assert f(None, None, None, None, None, 1, None, 2, 0, 128, 128, None) == 0
+
+
+@pytest.mark.skipif(gpu_available(), reason="only meaningful without a GPU (fake pointers)")
+def test_valid_call_without_gpu_reports_no_device():
+    L = _lib()
+    assert L.fp8q_quant_act_1x128(X, 4, 128, Q, SA, None) == 6
+    assert L.fp8_gemm_blockscaled(A, SA, B, SB, C, 1, 64, 128, 128, None) == 6
+
+
+def test_binding_names_match_c_abi():
+    import fp8_fine_grained_online_amd as pkg
+    for name in ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
+                 "fp8_gemm_grouped"]:
+        assert callable(getattr(pkg, name))
+
+
+def test_oracle_and_hip_path_share_no_code():
+    """Neither side imports the other; only the synthetic-input module is shared."""
+    pkg_dir = os.path.join(ROOT, "fp8_fine_grained_online_amd")
+    for dirpath, _, files in os.walk(pkg_dir):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), fn
+                assert "oracle/" not in text, fn
+    for fn in os.listdir(os.path.join(ROOT, "oracle")):
+        if fn.endswith(".py"):
+            text = open(os.path.join(ROOT, "oracle", fn)).read()
+            assert "fp8_fine_grained_online_amd" not in text, fn

@@ -1,0 +1,204 @@
+"""GPU parity of the block-scaled GEMM (dense and grouped) vs the oracle.
+
+Inputs are seeded bf16 tensors; the GPU quantizes them with its own kernels
+and multiplies; the oracle quantizes the same bytes and computes the exact
+per-group float64 result. Small shapes are compared element by element; the
+full-size workloads on sampled rows (every column). Outputs are NaN-poisoned
+before each call so that unwritten elements fail.
+"""
+
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from helpers import check_bf16, check_f32, from_dev_bf16_bits, mfma_bound, to_dev, to_dev_bf16
+from fp8_fine_grained_online_amd import synthetic as S
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def poisoned(shape, dtype):
+    import torch
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def gpu_pipeline(a_bits, b_bits, out, rows=None):
+    """GPU: quantize A and B, GEMM. Returns the output (host) for `rows`."""
+    import fp8_fine_grained_online_amd as F
+    import torch
+    qa, sa = F.fp8q_quant_act_1x128(to_dev_bf16(a_bits))
+    qb, sb = F.fp8q_quant_weight_128x128(to_dev_bf16(b_bits))
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    c = poisoned((a_bits.shape[0], b_bits.shape[0]), dt)
+    F.fp8_gemm_blockscaled(qa, sa, qb, sb, out, c=c)
+    torch.cuda.synchronize()
+    c = c if rows is None else c[torch.as_tensor(rows, device="cuda")]
+    return from_dev_bf16_bits(c) if out == "bf16" else c.cpu().numpy()
+
+
+def oracle_rows(a_bits, b_bits, rows=None):
+    """(C64, S, T) from the oracle's own quantization of the same bytes."""
+    from oracle import gemm, quant
+    a = a_bits if rows is None else a_bits[rows]
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant.quant_weight_128x128(b_bits)
+    return (gemm.gemm_blockscaled_f64(qa, sa, qb, sb), gemm.abs_sum(qa, sa, qb, sb),
+            mfma_bound(qa, sa, qb, sb))
+
+
+def check(got, c64, S_, T, out):
+    from oracle import bf16, gemm
+    if out == "f32":
+        return check_f32(got, c64, S_, T)
+    want = gemm.round_bf16(c64)
+    return check_bf16(got, c64, S_, T, want, bf16.ulp(want))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_small_workload_256x256x1024(out):
+    w = S.WORKLOADS["dense_256x256x1024"]
+    a, b = S.dense_inputs(w)
+    c64, S_, T = oracle_rows(a, b)
+    check(gpu_pipeline(a, b, out), c64, S_, T, out)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (100, 256, 384), (300, 384, 256),
+                                   (129, 128, 1024), (640, 512, 2048), (77, 1024, 7168)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_ragged_shapes(M, N, K, out):
+    a = S.activations(M, K, S.rng_for(800 + M, N))
+    b = S.weights(N, K, S.rng_for(800 + M, N + 1))
+    c64, S_, T = oracle_rows(a, b)
+    check(gpu_pipeline(a, b, out), c64, S_, T, out)
+
+
+def test_one_hot_layout():
+    """A single nonzero code pair lands at exactly (m0, n0) with the right scales.
+
+    Scales are powers of two, so every step is exact and the result must equal
+    the oracle bit for bit.
+    """
+    import fp8_fine_grained_online_amd as F
+    import torch
+    M, N, K = 160, 256, 384
+    rng = np.random.default_rng(1)
+    sa = np.exp2(rng.integers(-8, 8, (M, K // 128))).astype(np.float32)
+    sb = np.exp2(rng.integers(-8, 8, (N // 128, K // 128))).astype(np.float32)
+    from oracle import gemm
+    for m0, n0, k0 in [(0, 0, 0), (17, 129, 127), (159, 255, 383), (64, 16, 200), (130, 100, 255)]:
+        qa = np.zeros((M, K), np.uint8)
+        qb = np.zeros((N, K), np.uint8)
+        qa[m0, k0] = 0x3C
+        qb[n0, k0] = 0xC4
+        c = F.fp8_gemm_blockscaled(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), "f32",
+                                   c=poisoned((M, N), torch.float32))
+        torch.cuda.synchronize()
+        got = c.cpu().numpy().astype(np.float64)
+        want = gemm.gemm_blockscaled_f64(qa, sa, qb, sb)
+        assert np.array_equal(got, want), (m0, n0, k0, np.argwhere(got != want)[:3])
+
+
+def test_k_zero_writes_zeros_and_m_zero_is_noop():
+    import fp8_fine_grained_online_amd as F
+    import torch
+    a = torch.zeros((64, 0), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((64, 0), dtype=torch.float32, device="cuda")
+    b = torch.zeros((128, 0), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((1, 0), dtype=torch.float32, device="cuda")
+    c = F.fp8_gemm_blockscaled(a, sa, b, sb, "f32", c=poisoned((64, 128), torch.float32))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(c).item() == 0
+    a0 = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
+    c0 = F.fp8_gemm_blockscaled(a0, torch.zeros((0, 1), device="cuda"),
+                                torch.zeros((128, 128), dtype=torch.uint8, device="cuda"),
+                                torch.zeros((1, 1), device="cuda"), "bf16")
+    assert c0.shape == (0, 128)
+
+
+def test_deterministic_across_runs():
+    import fp8_fine_grained_online_amd as F
+    import torch
+    a = S.activations(512, 2048, S.rng_for(820, 0))
+    b = S.weights(512, 2048, S.rng_for(820, 1))
+    qa, sa = F.fp8q_quant_act_1x128(to_dev_bf16(a))
+    qb, sb = F.fp8q_quant_weight_128x128(to_dev_bf16(b))
+    c1 = F.fp8_gemm_blockscaled(qa, sa, qb, sb, "f32")
+    outs = [F.fp8_gemm_blockscaled(qa, sa, qb, sb, "f32") for _ in range(5)]
+    torch.cuda.synchronize()
+    for c in outs:
+        assert torch.equal(c, c1)
+
+
+FULL = ["dense_4096x4096x4096", "proj_8192x7168x2048", "proj_8192x2048x7168", "skinny_64x7168x7168"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    w = S.WORKLOADS[name]
+    a, b = S.dense_inputs(w)
+    rows = np.unique(np.concatenate([[0, w.M - 1], S.rng_for(830, w.wid).integers(0, w.M, 14)]))
+    got = gpu_pipeline(a, b, "bf16", rows=rows)
+    c64, S_, T = oracle_rows(a, b, rows)
+    check(got, c64, S_, T, "bf16")
+
+
+# ---------------------------------------------------------------- grouped
+
+def gpu_grouped(a_bits, b_bits, off, out):
+    import fp8_fine_grained_online_amd as F
+    import torch
+    qa, sa = F.fp8q_quant_act_1x128(to_dev_bf16(a_bits))
+    qb, sb = F.fp8q_quant_weight_128x128(to_dev_bf16(b_bits))
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    c = poisoned((a_bits.shape[0], b_bits.shape[1]), dt)
+    F.fp8_gemm_grouped(qa, sa, qb, sb, to_dev(np.asarray(off, np.int32)), out, c=c)
+    torch.cuda.synchronize()
+    return c
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_grouped_small_with_empty_experts_and_padding(out):
+    from oracle import gemm, quant
+    counts = np.array([100, 0, 300, 128, 1, 0])
+    padded = (counts + 127) // 128 * 128
+    off = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    G, N, K = len(counts), 256, 512
+    a = S.moe_activations(counts, off, K, S.rng_for(840, 0))
+    b = np.stack([S.weights(N, K, S.rng_for(840, 1 + e)) for e in range(G)])
+    c = gpu_grouped(a, b, off, out)
+    got = from_dev_bf16_bits(c) if out == "bf16" else c.cpu().numpy()
+    qa, sa = quant.quant_act_1x128(a)
+    qs = [quant.quant_weight_128x128(b[e]) for e in range(G)]
+    qb, sb = np.stack([x[0] for x in qs]), np.stack([x[1] for x in qs])
+    c64 = gemm.gemm_grouped_f64(qa, sa, qb, sb, off)
+    S_ = gemm.abs_sum_grouped(qa, sa, qb, sb, off)
+    T = np.zeros_like(S_)
+    for e in range(G):
+        r = slice(off[e], off[e + 1])
+        if off[e + 1] > off[e]:
+            T[r] = mfma_bound(qa[r], sa[r], qb[e], sb[e])
+    check(got, c64, S_, T, out)
+
+
+def test_grouped_full_size_sampled_experts():
+    """G=32, N=4096, K=7168, multinomial(65536) tokens padded to 128: 3 experts checked."""
+    import torch
+    from oracle import gemm, quant
+    w = S.WORKLOADS["moe_g32_65536x4096x7168"]
+    a, b, counts, off = S.grouped_inputs(w)
+    c = gpu_grouped(a, b, off, "bf16")
+    rng = S.rng_for(850, 0)
+    for e in [0, int(rng.integers(1, w.G - 1)), w.G - 1]:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 6)]))
+        got = from_dev_bf16_bits(c[torch.as_tensor(rows, device="cuda")])
+        qa, sa = quant.quant_act_1x128(a[rows])
+        qb, sb = quant.quant_weight_128x128(b[e])
+        c64 = gemm.gemm_blockscaled_f64(qa, sa, qb, sb)
+        S_ = gemm.abs_sum(qa, sa, qb, sb)
+        check(got, c64, S_, mfma_bound(qa, sa, qb, sb), "bf16")
+        # padding rows of this expert are exactly zero
+        if counts[e] < r1 - r0:
+            pad = c[r0 + int(counts[e]):r1].float()
+            assert torch.count_nonzero(pad).item() == 0
