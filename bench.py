@@ -74,6 +74,28 @@ def cpu_baseline(workload, a_bits, b_bits, rows):
     }
 
 
+def copy_calibration(steps, warmup):
+    """A plain 512 MiB device-to-device copy: bytes moved are known exactly."""
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 5),
+                      "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="dense_4096x4096x4096")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device-to-device copy of 512 MiB (HBM ceiling and the "
+                         "reference launch for calibrating FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -92,6 +117,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.steps, args.warmup)
+        return
 
     import fp8_fine_grained_online_amd as F
     from fp8_fine_grained_online_amd import synthetic as S
