@@ -25,11 +25,13 @@
 // 16-byte slots per wave instruction; each lane therefore fetches the global
 // chunk that belongs in its slot.
 //
-// Operand lanes: for the 16x16x128 MFMA, lane l supplies row l % 16 of the A
-// block (and row l % 16 of the B block, i.e. a column of B^T) with 32 bytes
-// of K. Which 32 of the 128 K bytes a lane carries only has to agree between A
-// and B: lane l takes chunks l/16 and 4 + l/16. Accumulator lanes: lane l
-// holds rows 4 (l/16) + r, r = 0..3, of column l % 16.
+// Operand lanes: for the 16x16x128 MFMA, lane l supplies row l % 16 of a
+// 16-row block of B (first operand) and of A (second operand) with 32 bytes of
+// K. Which 32 of the 128 K bytes a lane carries only has to agree between the
+// operands: lane l takes chunks l/16 and 4 + l/16. With B first, the MFMA
+// yields a block of C^T: lane l holds C[m = l % 16][n = 4 (l/16) + r],
+// r = 0..3, i.e. four consecutive columns of one row. So a lane needs one row
+// scale per block, and the epilogue stores 4 columns per lane at once.
 //
 // Ragged edges: the loads go through buffer descriptors sized to the tile's
 // valid rows, so rows past the end of A (or B) read as zeros; their results
@@ -107,6 +109,19 @@ __device__ __forceinline__ int xcd_tile(int id, int n) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// Tile index -> (row tile, column tile) in bands of kBand row tiles, column
+// by column within a band: a run of 32 consecutive tiles (one XCD's share of
+// a wave of workgroups) is a 4 x 8 block that reads 4 A slabs and 8 B slabs,
+// instead of 2 x 16 (2 A + 16 B slabs) in plain row-major order.
+constexpr int kBand = 4;
+__device__ __forceinline__ void band_tile(int t, int m_tiles, int n_tiles, int& tm, int& tn) {
+  const int band = t / (kBand * n_tiles);
+  const int local = t - band * kBand * n_tiles;
+  const int h = min(kBand, m_tiles - band * kBand);  // rows in this (possibly last) band
+  tn = local / h;
+  tm = band * kBand + local % h;
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kBf16Out, bool kGrouped>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kernel(GemmArgs p) {
   using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N>;
@@ -128,26 +143,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const uint8_t* bmat = p.b;
   const float* sbmat = p.sb;
   if constexpr (kGrouped) {
-    // tiles are numbered expert by expert: ceil(rows_e / BM) row tiles each
-    const int tile_m_global = tile / n_tiles_n;
-    tile_n = tile % n_tiles_n;
-    int e = 0, before = 0, lo = 0, hi = 0;
+    // tiles are numbered expert by expert (ceil(rows_e / BM) x n_tiles_n each),
+    // banded within an expert
+    int e = 0, before = 0, lo = 0, hi = 0, te = 0;
     for (; e < p.G; ++e) {
       lo = min(max(p.m_offsets[e], 0), p.M);
       hi = min(max(p.m_offsets[e + 1], lo), p.M);
-      const int t = (hi - lo + BM - 1) / BM;
-      if (tile_m_global < before + t) break;
-      before += t;
+      te = (hi - lo + BM - 1) / BM;
+      if (tile < before + te * n_tiles_n) break;
+      before += te * n_tiles_n;
     }
     if (e == p.G) return;  // beyond the last real tile (grid is an upper bound)
-    m0 = lo + (tile_m_global - before) * BM;
+    int tm;
+    band_tile(tile - before, te, n_tiles_n, tm, tile_n);
+    m0 = lo + tm * BM;
     m_end = min(m0 + BM, hi);
     bmat += (int64_t)e * p.N * p.K;
     sbmat += (int64_t)e * (p.N / kGroup) * G;
   } else {
-    const int tile_m = tile / n_tiles_n;
-    tile_n = tile % n_tiles_n;
-    m0 = tile_m * BM;
+    int tm;
+    band_tile(tile, (p.M + BM - 1) / BM, n_tiles_n, tm, tile_n);
+    m0 = tm * BM;
     m_end = min(m0 + BM, p.M);
   }
   const int n0 = tile_n * BN;
@@ -165,30 +181,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(p.a + (int64_t)m0 * p.K, (uint32_t)rows_a * (uint32_t)p.K);
   const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(bmat + (int64_t)n0 * p.K, (uint32_t)rows_b * (uint32_t)p.K);
   const __amdgpu_buffer_rsrc_t rsrc_sa = make_rsrc(p.sa + (int64_t)m0 * G, (uint32_t)rows_a * (uint32_t)G * 4);
-  uint32_t offa[Cfg::kLoadsA], offb[Cfg::kLoadsB];
-#pragma unroll
-  for (int i = 0; i < Cfg::kLoadsA; ++i) {
-    const int slot = i * Cfg::kThreads + tid;
-    const int row = slot >> 3, lc = (slot & 7) ^ (row & 7);
-    offa[i] = (uint32_t)row * (uint32_t)p.K + lc * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < Cfg::kLoadsB; ++i) {
-    const int slot = i * Cfg::kThreads + tid;
-    const int row = slot >> 3, lc = (slot & 7) ^ (row & 7);
-    offb[i] = (uint32_t)row * (uint32_t)p.K + lc * 16;
-  }
-  const uint32_t offsa = (uint32_t)tid * (uint32_t)G * 4;
+  // Slot q * kThreads + tid has row q * (kThreads / 8) + tid / 8 and stored
+  // chunk tid % 8, so copy q's per-lane offset is offa + q * row_step. The row
+  // part must stay in the per-lane offset: the buffer range check covers the
+  // per-lane offset but not the scalar one (which only carries the group's
+  // advance inside a row).
+  static_assert(Cfg::kThreads % 64 == 0, "row step keeps row % 8");
+  const int row0 = tid >> 3, lc0 = (tid & 7) ^ (row0 & 7);
+  const uint32_t offa = (uint32_t)row0 * (uint32_t)p.K + lc0 * 16;
+  const uint32_t offb = offa;
+  const uint32_t row_step = (uint32_t)(Cfg::kThreads / 8) * (uint32_t)p.K;
+  const uint32_t offsa = (uint32_t)(tid % BM) * (uint32_t)G * 4;
 
+  // Copy number q (0 .. kCopies-1) of this thread's share of group g into `stage`.
+  constexpr int kCopies = Cfg::kLoadsA + Cfg::kLoadsB + 1;
+  auto issue_copy = [&](int q, int g, uint8_t* __restrict__ stage) {
+    if (q < Cfg::kLoadsA) {
+      load_lds(rsrc_a, stage + (q * Cfg::kThreads + wave * 64) * 16, 16, offa + q * row_step,
+               g * kGroup);
+    } else if (q < Cfg::kLoadsA + Cfg::kLoadsB) {
+      const int i = q - Cfg::kLoadsA;
+      load_lds(rsrc_b, stage + Cfg::kLdsA + (i * Cfg::kThreads + wave * 64) * 16, 16,
+               offb + i * row_step, g * kGroup);
+    } else {
+      // waves past BM/64 repeat the copy of wave (wave % (BM/64)): same bytes,
+      // same place, and no wave-dependent branch in the step
+      load_lds(rsrc_sa, stage + Cfg::kLdsA + Cfg::kLdsB + (wave % (BM / 64)) * 64 * 4, 4, offsa, g * 4);
+    }
+  };
   auto issue_loads = [&](int g, uint8_t* __restrict__ stage) {
 #pragma unroll
-    for (int i = 0; i < Cfg::kLoadsA; ++i)
-      load_lds(rsrc_a, stage + (i * Cfg::kThreads + wave * 64) * 16, 16, offa[i], g * kGroup);
-#pragma unroll
-    for (int i = 0; i < Cfg::kLoadsB; ++i)
-      load_lds(rsrc_b, stage + Cfg::kLdsA + (i * Cfg::kThreads + wave * 64) * 16, 16, offb[i], g * kGroup);
-    if (wave < BM / 64)
-      load_lds(rsrc_sa, stage + Cfg::kLdsA + Cfg::kLdsB + wave * 64 * 4, 4, offsa, g * 4);
+    for (int q = 0; q < kCopies; ++q) issue_copy(q, g, stage);
   };
 
   v4f acc[SUBM][SUBN];
@@ -213,55 +236,73 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
 
-  // One K group from one LDS stage. sbv: this group's weight scale.
+  // One pipeline step: compute the K group held in `stage` (sbv: its weight
+  // scale) while copying group g_next into `nxt`. The restrict-qualified
+  // stages tell the compiler (and its wait-count pass) that the LDS reads of
+  // `stage` never alias the in-flight copies into `nxt`, so those copies are
+  // not waited on until the barrier.
   // The wave's SUBM x SUBN MFMAs run in sequence t = i * SUBN + j; the FMAs
   // promoting MFMA t-1 are issued right after MFMA t, so each promotion waits
   // on a result that is one MFMA old.
-  auto compute = [&](const uint8_t* __restrict__ stage, float sbv) {
+  //
+  // The copies of the next group are spread over the MFMAs (one every
+  // kCopyEvery MFMAs, pinned by scheduling-group hints): a wave issues in
+  // order, and a burst of direct-to-LDS copies would hold back its MFMAs
+  // while the memory pipeline accepts them.
+  constexpr int kCopyEvery = (SUBM * SUBN) / kCopies > 0 ? (SUBM * SUBN) / kCopies : 1;
+  auto step = [&](const uint8_t* __restrict__ stage, uint8_t* __restrict__ nxt, int g_next,
+                  float sbv) {
     const uint8_t* sA = stage;
     const uint8_t* sB = stage + Cfg::kLdsA;
-    const float* sSa = (const float*)(stage + Cfg::kLdsA + Cfg::kLdsB) + wm * WM + 4 * lk;
+    const float* sSa = (const float*)(stage + Cfg::kLdsA + Cfg::kLdsB) + wm * WM + lr;
     v8i bf[SUBN];
 #pragma unroll
     for (int j = 0; j < SUBN; ++j) bf[j] = load_frag(sB + (wn * WN + j * 16) * 128);
-    v8i af;
-    float4 sc, sc_prev;
+    // A fragment and A-scale of 16-row block i+1 are read while block i multiplies
+    v8i af = load_frag(sA + wm * WM * 128);
+    float sav = sSa[0];
+    v8i af_next;
+    float sav_next;
+    float sc, sc_prev;
     v4f part_prev;
 #pragma unroll
     for (int t = 0; t < SUBM * SUBN; ++t) {
       const int i = t / SUBN, j = t % SUBN;
+      if (t % kCopyEvery == 0 && t / kCopyEvery < kCopies) issue_copy(t / kCopyEvery, g_next, nxt);
       if (j == 0) {
-        af = load_frag(sA + (wm * WM + i * 16) * 128);
-        const float4 sav = *(const float4*)(sSa + i * 16);
-        sc = make_float4(sav.x * sbv, sav.y * sbv, sav.z * sbv, sav.w * sbv);
+        sc = sav * sbv;
+        if (i + 1 < SUBM) {
+          af_next = load_frag(sA + (wm * WM + (i + 1) * 16) * 128);
+          sav_next = sSa[(i + 1) * 16];
+        }
       }
       const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          af, bf[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          bf[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
       if (t > 0) {
         v4f& c = acc[(t - 1) / SUBN][(t - 1) % SUBN];
-        c[0] = __builtin_fmaf(part_prev[0], sc_prev.x, c[0]);
-        c[1] = __builtin_fmaf(part_prev[1], sc_prev.y, c[1]);
-        c[2] = __builtin_fmaf(part_prev[2], sc_prev.z, c[2]);
-        c[3] = __builtin_fmaf(part_prev[3], sc_prev.w, c[3]);
+        c[0] = __builtin_fmaf(part_prev[0], sc_prev, c[0]);
+        c[1] = __builtin_fmaf(part_prev[1], sc_prev, c[1]);
+        c[2] = __builtin_fmaf(part_prev[2], sc_prev, c[2]);
+        c[3] = __builtin_fmaf(part_prev[3], sc_prev, c[3]);
       }
       part_prev = part;
       sc_prev = sc;
+      if (j == SUBN - 1 && i + 1 < SUBM) {
+        af = af_next;
+        sav = sav_next;
+      }
     }
     v4f& c = acc[SUBM - 1][SUBN - 1];
-    c[0] = __builtin_fmaf(part_prev[0], sc_prev.x, c[0]);
-    c[1] = __builtin_fmaf(part_prev[1], sc_prev.y, c[1]);
-    c[2] = __builtin_fmaf(part_prev[2], sc_prev.z, c[2]);
-    c[3] = __builtin_fmaf(part_prev[3], sc_prev.w, c[3]);
-  };
-
-  // One pipeline step: copy group g_next into `nxt` while computing the group
-  // held in `cur`. The restrict-qualified stages tell the compiler (and its
-  // wait-count pass) that the LDS reads of `cur` never alias the in-flight
-  // copies into `nxt`, so the copies are not waited on until the barrier.
-  auto step = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, int g_next,
-                  float sbv) {
-    if (g_next < G) issue_loads(g_next, nxt);
-    compute(cur, sbv);
+    c[0] = __builtin_fmaf(part_prev[0], sc_prev, c[0]);
+    c[1] = __builtin_fmaf(part_prev[1], sc_prev, c[1]);
+    c[2] = __builtin_fmaf(part_prev[2], sc_prev, c[2]);
+    c[3] = __builtin_fmaf(part_prev[3], sc_prev, c[3]);
+    // scheduling hint: one copy, then kCopyEvery MFMAs, repeated
+#pragma unroll
+    for (int q = 0; q < kCopies; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // VMEM read (the copy)
+      __builtin_amdgcn_sched_group_barrier(0x008, kCopyEvery, 0);  // MFMA
+    }
   };
 
   // ---- main loop: group g computes from stage g % 2 while g+1 streams into the other ----
@@ -276,30 +317,163 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     uint8_t* cur = lds + (g & 1) * Cfg::kStage;
     uint8_t* nxt = lds + ((g + 1) & 1) * Cfg::kStage;
     const float sbv_next = (g + 1 < G) ? gsb[g + 1] : 0.0f;
-    step(cur, nxt, g + 1, sbv);
+    // the last group re-copies itself into the idle stage (never read): no branch in the step
+    step(cur, nxt, min(g + 1, G - 1), sbv);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this thread's copies have landed
     __syncthreads();                     // ... and everyone's; `cur` is free again
     sbv = sbv_next;
   }
 
-  // ---- epilogue ----
+  // ---- epilogue: each lane stores 4 consecutive columns of one row ----
 #pragma unroll
   for (int i = 0; i < SUBM; ++i) {
+    const int gm = m0 + wm * WM + i * 16 + lr;
+    if (gm >= m_end) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int gm = m0 + wm * WM + i * 16 + 4 * lk + r;
-      if (gm >= m_end) continue;
-#pragma unroll
-      for (int j = 0; j < SUBN; ++j) {
-        const int gn = n0 + wn * WN + j * 16 + lr;
-        if (gn >= p.N) continue;
-        const int64_t off = (int64_t)gm * p.N + gn;
-        if constexpr (kBf16Out) {
-          ((__bf16*)p.c)[off] = (__bf16)acc[i][j][r];
-        } else {
-          ((float*)p.c)[off] = acc[i][j][r];
-        }
+    for (int j = 0; j < SUBN; ++j) {
+      const int gn = n0 + wn * WN + j * 16 + 4 * lk;
+      if (gn >= p.N) continue;  // N % 128 == 0: a group of 4 columns is all in or all out
+      const int64_t off = (int64_t)gm * p.N + gn;
+      if constexpr (kBf16Out) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 v = {(__bf16)acc[i][j][0], (__bf16)acc[i][j][1], (__bf16)acc[i][j][2],
+                          (__bf16)acc[i][j][3]};
+        *(bf16x4*)((__bf16*)p.c + off) = v;
+      } else {
+        *(v4f*)((float*)p.c + off) = acc[i][j];
       }
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Small-M GEMM (HBM-bound shapes such as 64 x 7168 x 7168). A workgroup owns a
+// 64 x 32 block of C; its 8 waves split the K groups between them, each wave
+// streaming its B and A fragments straight from global memory into registers,
+// one group ahead, and promoting its own partial sums. The 8 partial blocks
+// are then summed through LDS (a fixed order, so results are deterministic)
+// and stored. B is read exactly once; A (small) is re-read per column block
+// from L2.
+// ---------------------------------------------------------------------------
+constexpr int kSkM = 64;     // rows per workgroup
+constexpr int kSkN = 32;     // columns per workgroup
+constexpr int kSkWaves = 8;  // K split inside the workgroup
+
+struct SkinnyFrags {
+  v8i b[kSkN / 16];
+  v8i a[kSkM / 16];
+  float sa[kSkM / 16];
+  float sb;
+};
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) float part[kSkWaves][(kSkM / 16) * (kSkN / 16)][64][4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lk = lane >> 4;
+  const int G = p.K / kGroup;
+  const int n_blocks = p.N / kSkN;
+  const int nb_idx = blockIdx.x % n_blocks;
+  const int m0 = (blockIdx.x / n_blocks) * kSkM;
+  const int n0 = nb_idx * kSkN;
+  const int m_last = min(m0 + kSkM, p.M) - 1;
+
+  // this wave's K groups: a contiguous range
+  const int g_begin = (int)((int64_t)G * wave / kSkWaves);
+  const int g_end = (int)((int64_t)G * (wave + 1) / kSkWaves);
+
+  const uint8_t* brow[kSkN / 16];
+  const uint8_t* arow[kSkM / 16];
+  const float* sarow[kSkM / 16];
+#pragma unroll
+  for (int jb = 0; jb < kSkN / 16; ++jb) brow[jb] = p.b + (int64_t)(n0 + jb * 16 + lr) * p.K + lk * 16;
+#pragma unroll
+  for (int ib = 0; ib < kSkM / 16; ++ib) {
+    const int m = min(m0 + ib * 16 + lr, m_last);  // rows past M: any valid row, never stored
+    arow[ib] = p.a + (int64_t)m * p.K + lk * 16;
+    sarow[ib] = p.sa + (int64_t)m * G;
+  }
+  const float* sbrow = p.sb + (int64_t)(n0 / kGroup) * G;
+
+  auto load = [&](int g, SkinnyFrags& f) {
+    const int64_t ko = (int64_t)g * kGroup;
+#pragma unroll
+    for (int jb = 0; jb < kSkN / 16; ++jb) {
+      const uint4 lo = *(const uint4*)(brow[jb] + ko);
+      const uint4 hi = *(const uint4*)(brow[jb] + ko + 64);
+      f.b[jb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int ib = 0; ib < kSkM / 16; ++ib) {
+      const uint4 lo = *(const uint4*)(arow[ib] + ko);
+      const uint4 hi = *(const uint4*)(arow[ib] + ko + 64);
+      f.a[ib] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      f.sa[ib] = sarow[ib][g];
+    }
+    f.sb = sbrow[g];
+  };
+
+  v4f acc[kSkM / 16][kSkN / 16];
+#pragma unroll
+  for (int ib = 0; ib < kSkM / 16; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < kSkN / 16; ++jb) acc[ib][jb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const SkinnyFrags& f) {
+#pragma unroll
+    for (int ib = 0; ib < kSkM / 16; ++ib) {
+      const float sc = f.sa[ib] * f.sb;
+#pragma unroll
+      for (int jb = 0; jb < kSkN / 16; ++jb) {
+        const v4f pp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            f.b[jb], f.a[ib], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        acc[ib][jb][0] = __builtin_fmaf(pp[0], sc, acc[ib][jb][0]);
+        acc[ib][jb][1] = __builtin_fmaf(pp[1], sc, acc[ib][jb][1]);
+        acc[ib][jb][2] = __builtin_fmaf(pp[2], sc, acc[ib][jb][2]);
+        acc[ib][jb][3] = __builtin_fmaf(pp[3], sc, acc[ib][jb][3]);
+      }
+    }
+  };
+
+  // two register stages: group g+1 is in flight while g is multiplied
+  SkinnyFrags f0, f1;
+  int g = g_begin;
+  if (g < g_end) load(g, f0);
+  for (; g + 1 < g_end; g += 2) {
+    load(g + 1, f1);
+    compute(f0);
+    if (g + 2 < g_end) load(g + 2, f0);
+    compute(f1);
+  }
+  if (g < g_end) compute(f0);
+
+  // ---- reduce the waves' partial blocks in LDS, in wave order ----
+#pragma unroll
+  for (int ib = 0; ib < kSkM / 16; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < kSkN / 16; ++jb)
+      *(v4f*)part[wave][ib * (kSkN / 16) + jb][lane] = acc[ib][jb];
+  __syncthreads();
+  constexpr int kBlocks = (kSkM / 16) * (kSkN / 16);
+  static_assert(kBlocks * 64 == 64 * kSkWaves, "one output quad per thread");
+  const int blk = tid >> 6;  // block of this thread's quad
+  v4f sum = *(const v4f*)part[0][blk][lane];
+#pragma unroll
+  for (int w = 1; w < kSkWaves; ++w) sum += *(const v4f*)part[w][blk][lane];
+  const int ib = blk / (kSkN / 16), jb = blk % (kSkN / 16);
+  const int gm = m0 + ib * 16 + lr;
+  const int gn = n0 + jb * 16 + 4 * lk;
+  if (gm < p.M) {
+    const int64_t off = (int64_t)gm * p.N + gn;
+    if constexpr (kBf16Out) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 v = {(__bf16)sum[0], (__bf16)sum[1], (__bf16)sum[2], (__bf16)sum[3]};
+      *(bf16x4*)((__bf16*)p.c + off) = v;
+    } else {
+      *(v4f*)((float*)p.c + off) = sum;
     }
   }
 }
@@ -320,10 +494,23 @@ static hipError_t launch_cfg(GemmArgs args, bool bf16_out, int m_tiles, hipStrea
   return hipGetLastError();
 }
 
+// Workgroups of the 256 x 256 kernel below which the small-M kernel is used:
+// fewer big tiles than this leave most of the 256 CUs idle.
+constexpr int64_t kSmallTileCount = 128;
+
 hipError_t launch_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
                                    const float* sb, void* c, bool bf16_out, int64_t M, int64_t N,
                                    int64_t K, hipStream_t stream) {
   GemmArgs args{a, sa, b, sb, c, nullptr, (int)M, (int)N, (int)K, 1, 0};
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles < kSmallTileCount) {
+    const dim3 grid((unsigned)(((M + kSkM - 1) / kSkM) * (N / kSkN)));
+    if (bf16_out)
+      hipLaunchKernelGGL(gemm_skinny_kernel<true>, grid, dim3(64 * kSkWaves), 0, stream, args);
+    else
+      hipLaunchKernelGGL(gemm_skinny_kernel<false>, grid, dim3(64 * kSkWaves), 0, stream, args);
+    return hipGetLastError();
+  }
   return launch_cfg<256, 256, 2, 4, false>(args, bf16_out, (int)((M + 255) / 256), stream);
 }
 
