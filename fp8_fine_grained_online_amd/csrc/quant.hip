@@ -9,6 +9,8 @@
 //
 // Both kernels are HBM-streaming: 2 bytes read, 1 byte + 4/128 bytes written
 // per element. Loads and stores are 16-byte / 8-byte per lane and coalesced.
+// The bf16 inputs are read once (non-temporal loads); the codes and scales are
+// stored normally so that the GEMM consuming them next finds them in cache.
 #include "common.hpp"
 
 namespace fp8q {
@@ -51,8 +53,7 @@ __global__ __launch_bounds__(kActThreads) void quant_act_1x128_kernel(
     out.x = pack4_e4m3(quotient(f[0], d), quotient(f[1], d), quotient(f[2], d), quotient(f[3], d));
     out.y = pack4_e4m3(quotient(f[4], d), quotient(f[5], d), quotient(f[6], d), quotient(f[7], d));
     if (c < n_chunks) {
-      __builtin_nontemporal_store(out.x, &q[c].x);
-      __builtin_nontemporal_store(out.y, &q[c].y);
+      q[c] = out;  // ordinary store: the GEMM reads the codes next, keep them cached
       if ((threadIdx.x & 15) == 0) sa[c >> 4] = s;
     }
   }
@@ -97,10 +98,7 @@ __global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
   const TileDivisor d = make_divisor(s, amax);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint2 out = quant8(v[i], d);
-    uint2* dst = q + c0 + (int64_t)i * 16 * chunks_per_row;
-    __builtin_nontemporal_store(out.x, &dst->x);
-    __builtin_nontemporal_store(out.y, &dst->y);
+    q[c0 + (int64_t)i * 16 * chunks_per_row] = quant8(v[i], d);
   }
   if (t == 0) sb[bn * nblk_k + bk] = s;
 }
