@@ -78,6 +78,42 @@ def abs_sum(qa, sa, qb, sb) -> np.ndarray:
     return s
 
 
+def gemm_rowscaled_f64(qa, sa, qb, sb_rows) -> np.ndarray:
+    """C = A * B^T with 1x128 scales on both operands (sb_rows: N x K/128).
+
+    The weight-gradient GEMM: both operands are activations/gradients
+    quantized per 1x128 tile along the reduction dimension, so the promotion
+    scale of group g is sa[m, g] * sb_rows[n, g].
+    """
+    M, K = qa.shape
+    N, K2 = qb.shape
+    if K != K2 or K % GROUP:
+        raise ValueError("shape mismatch: need A MxK, B NxK, K%128==0")
+    if sa.shape != (M, K // GROUP) or sb_rows.shape != (N, K // GROUP):
+        raise ValueError("scale shape mismatch")
+    a = e4m3.decode(qa)
+    b = e4m3.decode(qb)
+    sa64 = np.asarray(sa, dtype=np.float64)
+    sb64 = np.asarray(sb_rows, dtype=np.float64)
+    c = np.zeros((M, N), dtype=np.float64)
+    for g in range(K // GROUP):
+        ks = slice(g * GROUP, (g + 1) * GROUP)
+        c += (sa64[:, g][:, None] * sb64[:, g][None, :]) * (a[:, ks] @ b[:, ks].T)
+    return c
+
+
+def abs_sum_rowscaled(qa, sa, qb, sb_rows) -> np.ndarray:
+    M, K = qa.shape
+    a = np.abs(e4m3.decode(qa))
+    b = np.abs(e4m3.decode(qb))
+    s = np.zeros((M, qb.shape[0]), dtype=np.float64)
+    for g in range(K // GROUP):
+        ks = slice(g * GROUP, (g + 1) * GROUP)
+        s += (np.abs(np.asarray(sa[:, g], np.float64))[:, None]
+              * np.abs(np.asarray(sb_rows[:, g], np.float64))[None, :]) * (a[:, ks] @ b[:, ks].T)
+    return s
+
+
 def round_f32(c64: np.ndarray) -> np.ndarray:
     return np.asarray(c64, dtype=np.float64).astype(np.float32)
 

@@ -70,6 +70,60 @@ def quant_weight_128x128(w_bits: np.ndarray):
     return codes.reshape(N, K), s.reshape(N // GROUP, K // GROUP)
 
 
+def quant_act_128x1(x_bits: np.ndarray):
+    """Activations M x K (bf16 bits) in 128x1 tiles (128 consecutive rows of one
+    column), returned transposed: (codes uint8 K x M, scales float32 K x M/128).
+
+    The backward pass regroups activations from 1x128 to 128x1 tiles ("Six
+    Reasons Deepseek Ai Is A Waste Of Time", the sentence next to the Figure 7 (a)
+    passage); a 128x1 tile of X is a 1x128 tile of X^T, and the transposed layout
+    is the one a GEMM reducing over M consumes.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    if M % GROUP:
+        raise ValueError("M must be a multiple of 128")
+    return quant_act_1x128(np.ascontiguousarray(x_bits.T))
+
+
+def _quant_rows_f32(x32: np.ndarray):
+    """1x128 quantization of float32 rows (same rule as for bf16 inputs)."""
+    R, C = x32.shape
+    x = x32.reshape(R, C // GROUP, GROUP)
+    amax = np.max(np.abs(x), axis=2, keepdims=True)
+    codes, s = _quantize_groups(x, amax)
+    return codes.reshape(R, C), s.reshape(R, C // GROUP)
+
+
+def requant_1x128_to_128x1(codes: np.ndarray, scales: np.ndarray):
+    """Stored 1x128 FP8 activations -> 128x1 tiles, transposed (K x M codes).
+
+    The pages store the forward activations as 1x128 FP8 tiles and convert
+    them to 128x1 tiles for the backward pass ("Six Reasons Deepseek Ai Is A
+    Waste Of Time": the memory paragraph and the sentence next to Figure 7 (a)).
+    Reading: each element is dequantized to binary32, v = fl32(dec(q) * s)
+    (one rounding of the exact product), and v^T is quantized in 1x128 tiles
+    with the usual rule.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    M, K = codes.shape
+    if M % GROUP or K % GROUP:
+        raise ValueError("M and K must be multiples of 128")
+    v = (e4m3.decode(codes).reshape(M, K // GROUP, GROUP)
+         * np.asarray(scales, np.float64)[:, :, None]).astype(np.float32).reshape(M, K)
+    return _quant_rows_f32(np.ascontiguousarray(v.T))
+
+
+def transpose_weight_128x128(codes: np.ndarray, scales: np.ndarray):
+    """W (N x K codes, N/128 x K/128 scales) -> W^T (K x N codes, K/128 x N/128).
+
+    A 128x128 block of W is a 128x128 block of W^T with the same scale, so the
+    transpose is exact; it is the weight operand of the input-gradient GEMM.
+    """
+    return (np.ascontiguousarray(np.asarray(codes).T),
+            np.ascontiguousarray(np.asarray(scales, np.float32).T))
+
+
 def dequant_act(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """codes * s per 1x128 tile, exact in float64."""
     M, K = codes.shape
