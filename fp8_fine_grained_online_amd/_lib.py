@@ -49,6 +49,14 @@ def lib() -> ctypes.CDLL:
         L.fp8_gemm_blockscaled.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
         L.fp8_gemm_grouped.restype = i32
         L.fp8_gemm_grouped.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, vp]
+        L.fp8q_quant_act_128x1.restype = i32
+        L.fp8q_quant_act_128x1.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fp8q_requant_1x128_to_128x1.restype = i32
+        L.fp8q_requant_1x128_to_128x1.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        L.fp8q_transpose_weight_128x128.restype = i32
+        L.fp8q_transpose_weight_128x128.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        L.fp8_gemm_rowscaled.restype = i32
+        L.fp8_gemm_rowscaled.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
         _lib = L
     return _lib
 
@@ -188,4 +196,73 @@ def fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype="bf16", c=None, M_total=
     _check("fp8_gemm_grouped",
            lib().fp8_gemm_grouped(pa, psa, pb, psb, c.data_ptr(), code, poff, G, M, N, K,
                                   _stream(stream)))
+    return c
+
+
+def _div128(n):
+    return n // 128 if n % 128 == 0 else 0
+
+
+def fp8q_quant_act_128x1(x, qt=None, st=None, stream=None):
+    """x: bf16 M x K device tensor -> (qt uint8 K x M, st float32 K x M/128): 128x1 tiles, transposed."""
+    torch = _torch()
+    px = _dev(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    qt = _out(qt, "qt", (K, M), torch.uint8, x.device)
+    st = _out(st, "st", (K, _div128(M)), torch.float32, x.device)
+    _check("fp8q_quant_act_128x1",
+           lib().fp8q_quant_act_128x1(px, M, K, qt.data_ptr(), st.data_ptr(), _stream(stream)))
+    return qt, st
+
+
+def fp8q_requant_1x128_to_128x1(q, sa, qt=None, st=None, stream=None):
+    """Stored 1x128 codes q (M x K) and sa (M x K/128) -> (qt K x M, st K x M/128)."""
+    torch = _torch()
+    pq = _dev(q, "q", torch.uint8, 2)
+    psa = _dev(sa, "sa", torch.float32, 2)
+    M, K = q.shape
+    if tuple(sa.shape) != (M, _div128(K)):
+        raise ValueError("sa must have shape (M, K/128)")
+    qt = _out(qt, "qt", (K, M), torch.uint8, q.device)
+    st = _out(st, "st", (K, _div128(M)), torch.float32, q.device)
+    _check("fp8q_requant_1x128_to_128x1",
+           lib().fp8q_requant_1x128_to_128x1(pq, psa, M, K, qt.data_ptr(), st.data_ptr(),
+                                             _stream(stream)))
+    return qt, st
+
+
+def fp8q_transpose_weight_128x128(q, sb, qt=None, sbt=None, stream=None):
+    """Weight codes q (N x K) and block scales sb (N/128 x K/128) -> (qt K x N, sbt K/128 x N/128)."""
+    torch = _torch()
+    pq = _dev(q, "q", torch.uint8, 2)
+    psb = _dev(sb, "sb", torch.float32, 2)
+    N, K = q.shape
+    if tuple(sb.shape) != (_div128(N), _div128(K)):
+        raise ValueError("sb must have shape (N/128, K/128)")
+    qt = _out(qt, "qt", (K, N), torch.uint8, q.device)
+    sbt = _out(sbt, "sbt", (_div128(K), _div128(N)), torch.float32, q.device)
+    _check("fp8q_transpose_weight_128x128",
+           lib().fp8q_transpose_weight_128x128(pq, psb, N, K, qt.data_ptr(), sbt.data_ptr(),
+                                               _stream(stream)))
+    return qt, sbt
+
+
+def fp8_gemm_rowscaled(a, sa, b, sb, out_dtype="f32", c=None, stream=None):
+    """C = A * B^T with 1x128 scales on both operands: sa (M x K/128), sb (N x K/128)."""
+    torch = _torch()
+    code, tdt = _out_dtype(out_dtype)
+    pa = _dev(a, "a", torch.uint8, 2)
+    psa = _dev(sa, "sa", torch.float32, 2)
+    pb = _dev(b, "b", torch.uint8, 2)
+    psb = _dev(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if K % 128 == 0:
+        if tuple(sa.shape) != (M, K // 128) or tuple(sb.shape) != (N, K // 128):
+            raise ValueError("scale shapes must be (M, K/128) and (N, K/128)")
+    c = _out(c, "c", (M, N), tdt, a.device)
+    _check("fp8_gemm_rowscaled",
+           lib().fp8_gemm_rowscaled(pa, psa, pb, psb, c.data_ptr(), code, M, N, K, _stream(stream)))
     return c

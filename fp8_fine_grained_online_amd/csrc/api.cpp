@@ -21,12 +21,24 @@ hipError_t launch_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t*
                                const float* sb, void* c, bool bf16_out, const int32_t* m_offsets,
                                int64_t G, int64_t M_total, int64_t N, int64_t K,
                                hipStream_t stream);
+hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                 const float* sb_rows, void* c, bool bf16_out, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream);
+hipError_t launch_quant_act_128x1(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
+                                  hipStream_t stream);
+hipError_t launch_requant_1x128_to_128x1(const uint8_t* q, const float* sa, int64_t M, int64_t K,
+                                         uint8_t* qt, float* st, hipStream_t stream);
+hipError_t launch_transpose_weight_128x128(const uint8_t* q, const float* sb, int64_t N, int64_t K,
+                                           uint8_t* qt, float* sbt, hipStream_t stream);
 }  // namespace fp8q
 
 namespace {
 
 constexpr int64_t kGroup = 128;
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;  // kernels index rows/cols with int32
+// GEMM operand tiles (up to 256 rows of K bytes) are addressed with 32-bit
+// offsets through buffer descriptors
+constexpr int64_t kMaxK = int64_t(1) << 23;
 constexpr int kMaxDevices = 64;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -55,7 +67,7 @@ int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const
   if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
   if (N % kGroup || K % kGroup) return FP8Q_ERR_SHAPE;
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
-  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_TOO_LARGE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxK) return FP8Q_ERR_TOO_LARGE;
   if ((M + 127) / 128 * (N / 128) > kMaxDim) return FP8Q_ERR_TOO_LARGE;
   if (M == 0 || N == 0) return -1;  // valid no-op
   if (!c) return FP8Q_ERR_NULL;
@@ -66,11 +78,23 @@ int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const
   return FP8Q_OK;
 }
 
+// Checks shared by the three 128 x 128 tile re-tiling calls (R x C -> C x R).
+int check_retile(const void* in, const float* in_s, bool need_in_s, int64_t R, int64_t C,
+                 const uint8_t* out, const float* out_s) {
+  if (R < 0 || C < 0 || R % kGroup || C % kGroup) return FP8Q_ERR_SHAPE;
+  if (R > kMaxDim || C > kMaxDim || C / kGroup > 65535) return FP8Q_ERR_TOO_LARGE;
+  if (R == 0 || C == 0) return -1;  // valid no-op
+  if (!in || !out || !out_s || (need_in_s && !in_s)) return FP8Q_ERR_NULL;
+  if (!aligned(in, 16) || !aligned(out, 16) || !aligned(out_s, 4)) return FP8Q_ERR_ALIGN;
+  if (need_in_s && !aligned(in_s, 4)) return FP8Q_ERR_ALIGN;
+  return FP8Q_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fp8q_version(void) { return 100; }
+int fp8q_version(void) { return 200; }
 
 const char* fp8q_status_string(int status) {
   switch (status) {
@@ -132,6 +156,40 @@ int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b, const 
   if ((s = check_device())) return s;
   return launched(fp8q::launch_gemm_grouped(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16,
                                             m_offsets, G, M_total, N, K, (hipStream_t)stream));
+}
+
+int fp8q_quant_act_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* qt, float* st,
+                         void* stream) {
+  int s = check_retile(x_bf16, nullptr, false, M, K, qt, st);
+  if (s == -1) return FP8Q_OK;
+  if (s || (s = check_device())) return s;
+  return launched(fp8q::launch_quant_act_128x1(x_bf16, M, K, qt, st, (hipStream_t)stream));
+}
+
+int fp8q_requant_1x128_to_128x1(const uint8_t* q, const float* sa, int64_t M, int64_t K,
+                                uint8_t* qt, float* st, void* stream) {
+  int s = check_retile(q, sa, true, M, K, qt, st);
+  if (s == -1) return FP8Q_OK;
+  if (s || (s = check_device())) return s;
+  return launched(fp8q::launch_requant_1x128_to_128x1(q, sa, M, K, qt, st, (hipStream_t)stream));
+}
+
+int fp8q_transpose_weight_128x128(const uint8_t* q, const float* sb, int64_t N, int64_t K,
+                                  uint8_t* qt, float* sbt, void* stream) {
+  int s = check_retile(q, sb, true, N, K, qt, sbt);
+  if (s == -1) return FP8Q_OK;
+  if (s || (s = check_device())) return s;
+  return launched(fp8q::launch_transpose_weight_128x128(q, sb, N, K, qt, sbt, (hipStream_t)stream));
+}
+
+int fp8_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                       void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+  int s = check_gemm_common(a, sa, b, sb, c, out_dtype, M, N, K);
+  if (s == -1) return FP8Q_OK;
+  if (s) return s;
+  if ((s = check_device())) return s;
+  return launched(fp8q::launch_gemm_rowscaled(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16, M, N, K,
+                                              (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -37,6 +37,13 @@
 // valid rows, so rows past the end of A (or B) read as zeros; their results
 // are never stored.
 //
+// Row-scaled B (kRowB): for the weight-gradient GEMM both operands are
+// quantized in 1x128 tiles along K, so B carries one scale per row and group,
+// sb[n][g], and the promotion scale of each output element is
+// sa[m, g] * sb[n, g]. The tile's BN row scales of a group are staged in LDS
+// next to the A-scales, and each lane forms the four products of its four
+// columns per MFMA (four extra multiplies per MFMA).
+//
 // Tile order is XCD-aware: the hardware hands workgroup ids to the 8 XCDs
 // round-robin, so ids are remapped such that each XCD works on a contiguous
 // run of tiles (neighbouring tiles share A rows / B columns in its L2).
@@ -54,7 +61,7 @@ struct GemmArgs {
   const uint8_t* a;
   const float* sa;
   const uint8_t* b;
-  const float* sb;
+  const float* sb;           // 128x128 block scales, or N x G row scales (kRowB)
   void* c;
   const int32_t* m_offsets;  // grouped only
   int M;                     // rows of A / C (M_total when grouped)
@@ -64,7 +71,7 @@ struct GemmArgs {
   int n_tiles;  // number of real tiles (dense) / upper bound (grouped)
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kRowB = false>
 struct TileCfg {
   static constexpr int kWM = BM / WAVES_M;
   static constexpr int kWN = BN / WAVES_N;
@@ -74,13 +81,17 @@ struct TileCfg {
   static constexpr int kLdsA = BM * 128;  // bytes per stage
   static constexpr int kLdsB = BN * 128;
   static constexpr int kLdsSa = BM * 4;
-  static constexpr int kStage = kLdsA + kLdsB + kLdsSa;
+  static constexpr int kLdsSb = kRowB ? BN * 4 : 0;  // row scales of B (kRowB only)
+  static constexpr int kStage = kLdsA + kLdsB + kLdsSa + kLdsSb;
+  // waves copying one 64-scale panel each: BM/64 for A, BN/64 more for B's row scales
+  static constexpr int kScaleWaves = BM / 64 + (kRowB ? BN / 64 : 0);
   static constexpr int kLdsBytes = 2 * kStage;
   static constexpr int kLoadsA = BM * 8 / kThreads;  // 16-byte chunks per thread per group
   static constexpr int kLoadsB = BN * 8 / kThreads;
   static_assert(kWN <= 128 && 128 % kWN == 0, "a wave's columns must share one weight block");
   static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "whole wave loads");
-  static_assert(BM % 64 == 0 && BM <= kThreads, "A-scales: whole waves, one per thread");
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && kScaleWaves * 64 <= kThreads,
+                "scales: whole waves, one per thread");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
@@ -122,9 +133,10 @@ __device__ __forceinline__ void band_tile(int t, int m_tiles, int n_tiles, int& 
   tm = band * kBand + local % h;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool kBf16Out, bool kGrouped>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kBf16Out, bool kGrouped, bool kRowB>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kernel(GemmArgs p) {
-  using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N>;
+  using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N, kRowB>;
+  static_assert(!(kGrouped && kRowB), "row-scaled B is dense only");
   constexpr int WM = Cfg::kWM, WN = Cfg::kWN;
   constexpr int SUBM = Cfg::kSubM, SUBN = Cfg::kSubN;
   __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg::kLdsBytes];  // two stages
@@ -181,6 +193,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(p.a + (int64_t)m0 * p.K, (uint32_t)rows_a * (uint32_t)p.K);
   const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(bmat + (int64_t)n0 * p.K, (uint32_t)rows_b * (uint32_t)p.K);
   const __amdgpu_buffer_rsrc_t rsrc_sa = make_rsrc(p.sa + (int64_t)m0 * G, (uint32_t)rows_a * (uint32_t)G * 4);
+  // scale panels: wave w (mod kScaleWaves) copies 64 A-scales, or with kRowB
+  // 64 row scales of B, of each group (waves past kScaleWaves repeat a copy:
+  // same bytes, same place, and no wave-dependent branch in the step)
+  const int sw = wave % Cfg::kScaleWaves;
+  const bool sb_wave = kRowB && sw >= BM / 64;
+  const int s_panel = sb_wave ? sw - BM / 64 : sw;
+  __amdgpu_buffer_rsrc_t rsrc_s = rsrc_sa;
+  if constexpr (kRowB) {
+    if (sb_wave)
+      rsrc_s = make_rsrc(p.sb + (int64_t)n0 * G, (uint32_t)rows_b * (uint32_t)G * 4);
+  }
+  const int s_lds = Cfg::kLdsA + Cfg::kLdsB + (sb_wave ? Cfg::kLdsSa : 0) + s_panel * 64 * 4;
+  const uint32_t offs = (uint32_t)(s_panel * 64 + lane) * (uint32_t)G * 4;
   // Slot q * kThreads + tid has row q * (kThreads / 8) + tid / 8 and stored
   // chunk tid % 8, so copy q's per-lane offset is offa + q * row_step. The row
   // part must stay in the per-lane offset: the buffer range check covers the
@@ -191,7 +216,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const uint32_t offa = (uint32_t)row0 * (uint32_t)p.K + lc0 * 16;
   const uint32_t offb = offa;
   const uint32_t row_step = (uint32_t)(Cfg::kThreads / 8) * (uint32_t)p.K;
-  const uint32_t offsa = (uint32_t)(tid % BM) * (uint32_t)G * 4;
 
   // Copy number q (0 .. kCopies-1) of this thread's share of group g into `stage`.
   constexpr int kCopies = Cfg::kLoadsA + Cfg::kLoadsB + 1;
@@ -204,9 +228,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
       load_lds(rsrc_b, stage + Cfg::kLdsA + (i * Cfg::kThreads + wave * 64) * 16, 16,
                offb + i * row_step, g * kGroup);
     } else {
-      // waves past BM/64 repeat the copy of wave (wave % (BM/64)): same bytes,
-      // same place, and no wave-dependent branch in the step
-      load_lds(rsrc_sa, stage + Cfg::kLdsA + Cfg::kLdsB + (wave % (BM / 64)) * 64 * 4, 4, offsa, g * 4);
+      load_lds(rsrc_s, stage + s_lds, 4, offs, g * 4);
     }
   };
   auto issue_loads = [&](int g, uint8_t* __restrict__ stage) {
@@ -250,6 +272,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   // order, and a burst of direct-to-LDS copies would hold back its MFMAs
   // while the memory pipeline accepts them.
   constexpr int kCopyEvery = (SUBM * SUBN) / kCopies > 0 ? (SUBM * SUBN) / kCopies : 1;
+  // acc += part * scale: one scale for the lane's four columns (128x128 B
+  // blocks: sc1 = sa * sb), or one per column (kRowB: sa * sb_row, formed
+  // here so that no per-column products stay live across MFMAs)
+  auto promote = [](v4f& c, const v4f& part, float sc1, float sa1, const v4f& sbr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c[r] = __builtin_fmaf(part[r], kRowB ? sbr[r] * sa1 : sc1, c[r]);
+  };
   auto step = [&](const uint8_t* __restrict__ stage, uint8_t* __restrict__ nxt, int g_next,
                   float sbv) {
     const uint8_t* sA = stage;
@@ -258,12 +287,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     v8i bf[SUBN];
 #pragma unroll
     for (int j = 0; j < SUBN; ++j) bf[j] = load_frag(sB + (wn * WN + j * 16) * 128);
+    // kRowB: the row scales of the lane's four columns in each 16-column block
+    v4f sbq[kRowB ? SUBN : 1];
+    if constexpr (kRowB) {
+      const float* sSb = (const float*)(stage + Cfg::kLdsA + Cfg::kLdsB + Cfg::kLdsSa) + wn * WN + 4 * lk;
+#pragma unroll
+      for (int j = 0; j < SUBN; ++j) sbq[j] = *(const v4f*)(sSb + j * 16);
+    }
     // A fragment and A-scale of 16-row block i+1 are read while block i multiplies
     v8i af = load_frag(sA + wm * WM * 128);
     float sav = sSa[0];
     v8i af_next;
     float sav_next;
     float sc, sc_prev;
+    float sav_prev;  // kRowB: A-scale of the previous 16-row block
     v4f part_prev;
 #pragma unroll
     for (int t = 0; t < SUBM * SUBN; ++t) {
@@ -278,25 +315,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
       }
       const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           bf[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      if (t > 0) {
-        v4f& c = acc[(t - 1) / SUBN][(t - 1) % SUBN];
-        c[0] = __builtin_fmaf(part_prev[0], sc_prev, c[0]);
-        c[1] = __builtin_fmaf(part_prev[1], sc_prev, c[1]);
-        c[2] = __builtin_fmaf(part_prev[2], sc_prev, c[2]);
-        c[3] = __builtin_fmaf(part_prev[3], sc_prev, c[3]);
-      }
+      // MFMA t-1 belongs to the previous 16-row block exactly when j == 0
+      if (t > 0)
+        promote(acc[(t - 1) / SUBN][(t - 1) % SUBN], part_prev, sc_prev, j == 0 ? sav_prev : sav,
+                sbq[kRowB ? (t - 1) % SUBN : 0]);
       part_prev = part;
       sc_prev = sc;
       if (j == SUBN - 1 && i + 1 < SUBM) {
         af = af_next;
+        sav_prev = sav;
         sav = sav_next;
       }
     }
-    v4f& c = acc[SUBM - 1][SUBN - 1];
-    c[0] = __builtin_fmaf(part_prev[0], sc_prev, c[0]);
-    c[1] = __builtin_fmaf(part_prev[1], sc_prev, c[1]);
-    c[2] = __builtin_fmaf(part_prev[2], sc_prev, c[2]);
-    c[3] = __builtin_fmaf(part_prev[3], sc_prev, c[3]);
+    promote(acc[SUBM - 1][SUBN - 1], part_prev, sc_prev, sav, sbq[kRowB ? SUBN - 1 : 0]);
     // scheduling hint: one copy, then kCopyEvery MFMAs, repeated
 #pragma unroll
     for (int q = 0; q < kCopies; ++q) {
@@ -308,7 +339,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   // ---- main loop: group g computes from stage g % 2 while g+1 streams into the other ----
   float sbv = 0.0f;
   if (G > 0) {
-    sbv = gsb[0];
+    if constexpr (!kRowB) sbv = gsb[0];
     issue_loads(0, lds);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -316,7 +347,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   for (int g = 0; g < G; ++g) {
     uint8_t* cur = lds + (g & 1) * Cfg::kStage;
     uint8_t* nxt = lds + ((g + 1) & 1) * Cfg::kStage;
-    const float sbv_next = (g + 1 < G) ? gsb[g + 1] : 0.0f;
+    const float sbv_next = (!kRowB && g + 1 < G) ? gsb[g + 1] : 0.0f;
     // the last group re-copies itself into the idle stage (never read): no branch in the step
     step(cur, nxt, min(g + 1, G - 1), sbv);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this thread's copies have landed
@@ -367,7 +398,15 @@ struct SkinnyFrags {
   float sb;
 };
 
-template <bool kBf16Out>
+// kRowB: the row scales of the lane's four columns in each 16-column block
+template <bool kRowB>
+struct SkinnyRowScales {
+  v4f sb[kSkN / 16];
+};
+template <>
+struct SkinnyRowScales<false> {};
+
+template <bool kBf16Out, bool kRowB>
 __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) float part[kSkWaves][(kSkM / 16) * (kSkN / 16)][64][4];
   const int tid = threadIdx.x;
@@ -379,41 +418,65 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs p) 
   const int nb_idx = blockIdx.x % n_blocks;
   const int m0 = (blockIdx.x / n_blocks) * kSkM;
   const int n0 = nb_idx * kSkN;
-  const int m_last = min(m0 + kSkM, p.M) - 1;
 
   // this wave's K groups: a contiguous range
   const int g_begin = (int)((int64_t)G * wave / kSkWaves);
   const int g_end = (int)((int64_t)G * (wave + 1) / kSkWaves);
 
-  const uint8_t* brow[kSkN / 16];
-  const uint8_t* arow[kSkM / 16];
-  const float* sarow[kSkM / 16];
-#pragma unroll
-  for (int jb = 0; jb < kSkN / 16; ++jb) brow[jb] = p.b + (int64_t)(n0 + jb * 16 + lr) * p.K + lk * 16;
+  // Operands through buffer descriptors over the workgroup's rows, with
+  // 32-bit per-lane row offsets and the group's advance inside a row as the
+  // scalar offset (the range check covers the per-lane part, so A rows past
+  // M read as zeros; their outputs are never stored). All kSkN B rows exist
+  // (N % 128 == 0).
+  const int rows_a = min(kSkM, p.M - m0);
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(p.a + (int64_t)m0 * p.K, (uint32_t)rows_a * (uint32_t)p.K);
+  const __amdgpu_buffer_rsrc_t rsrc_sa = make_rsrc(p.sa + (int64_t)m0 * G, (uint32_t)rows_a * (uint32_t)G * 4);
+  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(p.b + (int64_t)n0 * p.K, (uint32_t)kSkN * (uint32_t)p.K);
+  // block scales: the G scales of weight block n0 / 128; row scales (kRowB):
+  // rows n0 .. n0 + kSkN - 1, G each
+  const __amdgpu_buffer_rsrc_t rsrc_sb =
+      kRowB ? make_rsrc(p.sb + (int64_t)n0 * G, (uint32_t)kSkN * (uint32_t)G * 4)
+            : make_rsrc(p.sb + (int64_t)(n0 / kGroup) * G, (uint32_t)G * 4);
+  uint32_t a_off[kSkM / 16], sa_off[kSkM / 16], b_off[kSkN / 16];
 #pragma unroll
   for (int ib = 0; ib < kSkM / 16; ++ib) {
-    const int m = min(m0 + ib * 16 + lr, m_last);  // rows past M: any valid row, never stored
-    arow[ib] = p.a + (int64_t)m * p.K + lk * 16;
-    sarow[ib] = p.sa + (int64_t)m * G;
+    a_off[ib] = (uint32_t)(ib * 16 + lr) * (uint32_t)p.K + lk * 16;
+    sa_off[ib] = (uint32_t)(ib * 16 + lr) * (uint32_t)G * 4;
   }
-  const float* sbrow = p.sb + (int64_t)(n0 / kGroup) * G;
-
-  auto load = [&](int g, SkinnyFrags& f) {
-    const int64_t ko = (int64_t)g * kGroup;
 #pragma unroll
-    for (int jb = 0; jb < kSkN / 16; ++jb) {
-      const uint4 lo = *(const uint4*)(brow[jb] + ko);
-      const uint4 hi = *(const uint4*)(brow[jb] + ko + 64);
-      f.b[jb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+  for (int jb = 0; jb < kSkN / 16; ++jb) b_off[jb] = (uint32_t)(jb * 16 + lr) * (uint32_t)p.K + lk * 16;
+  // kRowB: the lane's columns are n0 + 16 jb + 4 lk + r, r = 0..3
+  const uint32_t sbr_off = (uint32_t)(4 * lk) * (uint32_t)G * 4;
+  const uint32_t sb_row_step = (uint32_t)G * 4;
+
+  auto frag = [](u32x4 lo, u32x4 hi) {
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto load = [&](int g, SkinnyFrags& f, SkinnyRowScales<kRowB>& fr) {
+    const int ko = g * kGroup;
+#pragma unroll
+    for (int jb = 0; jb < kSkN / 16; ++jb)
+      f.b[jb] = frag(__builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[jb], ko, 0),
+                     __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[jb], ko + 64, 0));
 #pragma unroll
     for (int ib = 0; ib < kSkM / 16; ++ib) {
-      const uint4 lo = *(const uint4*)(arow[ib] + ko);
-      const uint4 hi = *(const uint4*)(arow[ib] + ko + 64);
-      f.a[ib] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      f.sa[ib] = sarow[ib][g];
+      f.a[ib] = frag(__builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[ib], ko, 0),
+                     __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[ib], ko + 64, 0));
+      f.sa[ib] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_sa, sa_off[ib], g * 4, 0));
     }
-    f.sb = sbrow[g];
+    if constexpr (kRowB) {
+#pragma unroll
+      for (int jb = 0; jb < kSkN / 16; ++jb) {
+        v4f v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rsrc_sb, sbr_off, (jb * 16 + r) * sb_row_step + g * 4, 0));
+        fr.sb[jb] = v;
+      }
+    } else {
+      f.sb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_sb, 0, g * 4, 0));
+    }
   };
 
   v4f acc[kSkM / 16][kSkN / 16];
@@ -422,33 +485,40 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs p) 
 #pragma unroll
     for (int jb = 0; jb < kSkN / 16; ++jb) acc[ib][jb] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const SkinnyFrags& f) {
+  auto compute = [&](const SkinnyFrags& f, const SkinnyRowScales<kRowB>& fr) {
 #pragma unroll
     for (int ib = 0; ib < kSkM / 16; ++ib) {
-      const float sc = f.sa[ib] * f.sb;
 #pragma unroll
       for (int jb = 0; jb < kSkN / 16; ++jb) {
+        v4f sc;
+        if constexpr (kRowB) {
+          sc = fr.sb[jb] * f.sa[ib];
+        } else {
+          const float s1 = f.sa[ib] * f.sb;
+          sc = v4f{s1, s1, s1, s1};
+        }
         const v4f pp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             f.b[jb], f.a[ib], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        acc[ib][jb][0] = __builtin_fmaf(pp[0], sc, acc[ib][jb][0]);
-        acc[ib][jb][1] = __builtin_fmaf(pp[1], sc, acc[ib][jb][1]);
-        acc[ib][jb][2] = __builtin_fmaf(pp[2], sc, acc[ib][jb][2]);
-        acc[ib][jb][3] = __builtin_fmaf(pp[3], sc, acc[ib][jb][3]);
+        acc[ib][jb][0] = __builtin_fmaf(pp[0], sc[0], acc[ib][jb][0]);
+        acc[ib][jb][1] = __builtin_fmaf(pp[1], sc[1], acc[ib][jb][1]);
+        acc[ib][jb][2] = __builtin_fmaf(pp[2], sc[2], acc[ib][jb][2]);
+        acc[ib][jb][3] = __builtin_fmaf(pp[3], sc[3], acc[ib][jb][3]);
       }
     }
   };
 
   // two register stages: group g+1 is in flight while g is multiplied
   SkinnyFrags f0, f1;
+  SkinnyRowScales<kRowB> r0, r1;
   int g = g_begin;
-  if (g < g_end) load(g, f0);
+  if (g < g_end) load(g, f0, r0);
   for (; g + 1 < g_end; g += 2) {
-    load(g + 1, f1);
-    compute(f0);
-    if (g + 2 < g_end) load(g + 2, f0);
-    compute(f1);
+    load(g + 1, f1, r1);
+    compute(f0, r0);
+    if (g + 2 < g_end) load(g + 2, f0, r0);
+    compute(f1, r1);
   }
-  if (g < g_end) compute(f0);
+  if (g < g_end) compute(f0, r0);
 
   // ---- reduce the waves' partial blocks in LDS, in wave order ----
 #pragma unroll
@@ -478,18 +548,18 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs p) 
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool kGrouped>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kGrouped, bool kRowB>
 static hipError_t launch_cfg(GemmArgs args, bool bf16_out, int m_tiles, hipStream_t stream) {
-  using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N>;
+  using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N, kRowB>;
   args.n_tiles = m_tiles * ((args.N + BN - 1) / BN);
   const dim3 grid((unsigned)args.n_tiles);
   const dim3 block(Cfg::kThreads);
   if (bf16_out) {
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, true, kGrouped>), grid,
-                       block, 0, stream, args);
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, true, kGrouped, kRowB>),
+                       grid, block, 0, stream, args);
   } else {
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, false, kGrouped>), grid,
-                       block, 0, stream, args);
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, false, kGrouped, kRowB>),
+                       grid, block, 0, stream, args);
   }
   return hipGetLastError();
 }
@@ -498,20 +568,39 @@ static hipError_t launch_cfg(GemmArgs args, bool bf16_out, int m_tiles, hipStrea
 // fewer big tiles than this leave most of the 256 CUs idle.
 constexpr int64_t kSmallTileCount = 128;
 
-hipError_t launch_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
-                                   const float* sb, void* c, bool bf16_out, int64_t M, int64_t N,
-                                   int64_t K, hipStream_t stream) {
-  GemmArgs args{a, sa, b, sb, c, nullptr, (int)M, (int)N, (int)K, 1, 0};
+template <bool kRowB>
+static hipError_t launch_dense(GemmArgs args, bool bf16_out, hipStream_t stream) {
+  const int64_t M = args.M, N = args.N;
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (big_tiles < kSmallTileCount) {
     const dim3 grid((unsigned)(((M + kSkM - 1) / kSkM) * (N / kSkN)));
     if (bf16_out)
-      hipLaunchKernelGGL(gemm_skinny_kernel<true>, grid, dim3(64 * kSkWaves), 0, stream, args);
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, kRowB>), grid, dim3(64 * kSkWaves), 0, stream, args);
     else
-      hipLaunchKernelGGL(gemm_skinny_kernel<false>, grid, dim3(64 * kSkWaves), 0, stream, args);
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, kRowB>), grid, dim3(64 * kSkWaves), 0, stream, args);
     return hipGetLastError();
   }
-  return launch_cfg<256, 256, 2, 4, false>(args, bf16_out, (int)((M + 255) / 256), stream);
+  // Row-scaled B holds WN/4 column scales per lane through a step; a 64x64
+  // wave tile (256 x 128 workgroup tile) keeps that within the registers of
+  // two waves per SIMD.
+  if constexpr (kRowB)
+    return launch_cfg<256, 128, 4, 2, false, true>(args, bf16_out, (int)((M + 255) / 256), stream);
+  else
+    return launch_cfg<256, 256, 2, 4, false, false>(args, bf16_out, (int)((M + 255) / 256), stream);
+}
+
+hipError_t launch_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                   const float* sb, void* c, bool bf16_out, int64_t M, int64_t N,
+                                   int64_t K, hipStream_t stream) {
+  return launch_dense<false>(GemmArgs{a, sa, b, sb, c, nullptr, (int)M, (int)N, (int)K, 1, 0},
+                             bf16_out, stream);
+}
+
+hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                 const float* sb_rows, void* c, bool bf16_out, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream) {
+  return launch_dense<true>(GemmArgs{a, sa, b, sb_rows, c, nullptr, (int)M, (int)N, (int)K, 1, 0},
+                            bf16_out, stream);
 }
 
 hipError_t launch_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b,
@@ -521,7 +610,7 @@ hipError_t launch_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t*
   GemmArgs args{a, sa, b, sb, c, m_offsets, (int)M_total, (int)N, (int)K, (int)G, 0};
   // upper bound on sum_e ceil(rows_e / 256) for rows_e multiples of 128
   const int64_t m_tiles = (M_total / 128 + G + 1) / 2;
-  return launch_cfg<256, 256, 2, 4, true>(args, bf16_out, (int)m_tiles, stream);
+  return launch_cfg<256, 256, 2, 4, true, false>(args, bf16_out, (int)m_tiles, stream);
 }
 
 }  // namespace fp8q

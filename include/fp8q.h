@@ -38,6 +38,9 @@
  *    caller's next synchronization. Nothing aborts, throws or prints.
  *  - Non-finite inputs are outside the contract (codes and outputs are then
  *    unspecified, but every kernel still terminates).
+ *  - Size limits (FP8Q_ERR_TOO_LARGE beyond them): every dimension below 2^31;
+ *    the GEMMs' reduction dimension K at most 2^23 (operand tiles are
+ *    addressed with 32-bit offsets).
  */
 #ifndef FP8Q_H
 #define FP8Q_H
@@ -148,6 +151,103 @@ FP8Q_API int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8
 FP8Q_API int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                      void* c, int out_dtype, const int32_t* m_offsets, int64_t G,
                      int64_t M_total, int64_t N, int64_t K, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Backward pass of a linear layer Y = X W^T (X: M tokens x K in-channels,
+ * W: N out-channels x K). "Six Reasons Deepseek Ai Is A Waste Of Time": the
+ * GEMM-operands paragraph (Fprop, Dgrad and Wgrad all in E4M3) and the
+ * Figure 7 (a) passage (activations converted from 1x128 to 128x1 tiles for
+ * the backward pass); woojincopolymer.co.kr post, memory paragraph (the
+ * forward activations are stored as 1x128 FP8 tiles).
+ *
+ *   Dgrad  dX = dY W    : fp8q_quant_act_1x128(dY) and
+ *                         fp8q_transpose_weight_128x128(W) feed
+ *                         fp8_gemm_blockscaled (A = dY, B = W^T, K = N).
+ *   Wgrad  dW = dY^T X  : fp8q_quant_act_128x1(dY) and
+ *                         fp8q_requant_1x128_to_128x1(stored X) feed
+ *                         fp8_gemm_rowscaled (A = dY^T, B = X^T, K = M).
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * 128x1 activation quantization, output transposed.
+ * Source: the Figure 7 (a) passage of "Six Reasons Deepseek Ai Is A Waste Of
+ * Time" (128x1 tiles in the backward pass), with the quantization rule of
+ * fp8q_quant_act_1x128.
+ *
+ * A 128x1 tile is 128 consecutive rows of one column of x. For each column k
+ * and row group r (rows 128r .. 128r+127):
+ *   amax = max |x[128r .. 128r+127, k]|, s = fl32(amax / 448),
+ *   qt[k, m] = E4M3_RNE(clamp(fl32(x[m, k] / s), -448, 448)),  st[k, r] = s.
+ * i.e. the 1x128 quantization of x^T.
+ *
+ *   x_bf16 : in,  M x K bfloat16, 16-byte aligned
+ *   qt     : out, K x M E4M3 bytes (x^T), 16-byte aligned
+ *   st     : out, K x (M/128) float32, 4-byte aligned
+ * Requires M % 128 == 0 and K % 128 == 0. M == 0 or K == 0 is a no-op.
+ */
+FP8Q_API int fp8q_quant_act_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* qt, float* st,
+                                  void* stream);
+
+/*
+ * Re-tiling of stored 1x128 FP8 activations into 128x1 tiles, transposed.
+ * Source: the Figure 7 (a) passage of "Six Reasons Deepseek Ai Is A Waste Of
+ * Time" (conversion from 1x128 to 128x1 tiles) and the memory paragraph of
+ * the woojincopolymer.co.kr post (the stored form is 1x128 FP8).
+ *
+ * Each element is dequantized to binary32 with one rounding,
+ *   v[m, k] = fl32(dec(q[m, k]) * sa[m, k/128]),
+ * and v is quantized in 128x1 tiles exactly as fp8q_quant_act_128x1 does
+ * (amax over 128 rows of a column, s = fl32(amax/448), codes of fl32(v/s)).
+ *
+ *   q  : in,  M x K E4M3 (from fp8q_quant_act_1x128), 16-byte aligned
+ *   sa : in,  M x (K/128) float32; every dec(q) * sa must be finite in
+ *        binary32 (true for any output of fp8q_quant_act_1x128 on finite
+ *        input: |dec(q)| <= 448 and sa <= FLT_MAX / 448)
+ *   qt : out, K x M E4M3, 16-byte aligned
+ *   st : out, K x (M/128) float32
+ * Requires M % 128 == 0 and K % 128 == 0. M == 0 or K == 0 is a no-op.
+ */
+FP8Q_API int fp8q_requant_1x128_to_128x1(const uint8_t* q, const float* sa, int64_t M, int64_t K,
+                                         uint8_t* qt, float* st, void* stream);
+
+/*
+ * Transpose of 128x128-block-quantized weights: W (N x K) -> W^T (K x N).
+ * A 128x128 block of W is a 128x128 block of W^T with the same maximum, so
+ * the transposed codes and scales are exactly those of quantizing W^T; the
+ * result is the weight operand of the Dgrad GEMM. Source: the Figure 7 (a)
+ * passage of "Six Reasons Deepseek Ai Is A Waste Of Time" (128x128 blocks)
+ * and its GEMM-operands paragraph (Dgrad in E4M3).
+ *
+ *   q   : in,  N x K E4M3, 16-byte aligned
+ *   sb  : in,  (N/128) x (K/128) float32
+ *   qt  : out, K x N E4M3, 16-byte aligned
+ *   sbt : out, (K/128) x (N/128) float32
+ * Requires N % 128 == 0 and K % 128 == 0. N == 0 or K == 0 is a no-op.
+ */
+FP8Q_API int fp8q_transpose_weight_128x128(const uint8_t* q, const float* sb, int64_t N, int64_t K,
+                                           uint8_t* qt, float* sbt, void* stream);
+
+/*
+ * FP8 GEMM with 1x128 scales on both operands (the Wgrad GEMM): C = A * B^T,
+ *   acc[m, n] += (sa[m, g] * sb[n, g]) * P_g[m, n],
+ * with P_g and the promotion as in fp8_gemm_blockscaled. Source: the
+ * GEMM-operands paragraph (Wgrad in E4M3) and the paragraphs on fine-grained
+ * quantization and promotion of "Six Reasons Deepseek Ai Is A Waste Of Time";
+ * both operands are activations/gradients quantized along the reduction
+ * dimension (the 128x1 tiles of the Figure 7 (a) passage, stored transposed).
+ *
+ *   a  : in,  M x K E4M3, 16-byte aligned   (Wgrad: dY^T, M = out-channels)
+ *   sa : in,  M x (K/128) float32
+ *   b  : in,  N x K E4M3, 16-byte aligned   (Wgrad: X^T, N = in-channels)
+ *   sb : in,  N x (K/128) float32 (one scale per row and group)
+ *   c  : out, M x N, float32 or bfloat16, 16-byte aligned
+ * Requires N % 128 == 0 and K % 128 == 0; M is arbitrary. M == 0 or N == 0
+ * is a no-op; K == 0 writes zeros (a, sa, b, sb may then be NULL).
+ */
+FP8Q_API int fp8_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                                void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream);
 
 #ifdef __cplusplus
 }

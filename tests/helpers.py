@@ -52,14 +52,19 @@ def e4m3_exponent(codes):
     return np.where((c & 0x7F) == 0, NO_EXP, np.where(e == 0, -6, e - 7))
 
 
-def mfma_bound(qa, sa, qb, sb):
-    """T (M x N): bound on the FP8 matrix cores' truncation, see module docstring."""
+def mfma_bound(qa, sa, qb, sb, row_scales=False):
+    """T (M x N): bound on the FP8 matrix cores' truncation, see module docstring.
+
+    sb holds 128x128 block scales (N/128 x K/128), or with row_scales one
+    scale per row of B and group (N x K/128).
+    """
     ea = e4m3_exponent(qa)
     eb = e4m3_exponent(qb)
     M, K = ea.shape
     N = eb.shape[0]
     sa64 = np.abs(np.asarray(sa, np.float64))
-    sb_rows = np.repeat(np.abs(np.asarray(sb, np.float64)), 128, axis=0)
+    sb64 = np.abs(np.asarray(sb, np.float64))
+    sb_rows = sb64 if row_scales else np.repeat(sb64, 128, axis=0)
     out = np.zeros((M, N))
     for g in range(K // 128):
         acc = np.zeros((M, N))

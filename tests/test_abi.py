@@ -24,10 +24,14 @@ def declared_symbols():
     return re.findall(r"FP8Q_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
 
 
-def test_header_declares_the_four_entry_points():
+ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
+                "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
+                "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled"]
+
+
+def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    for name in ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
-                 "fp8_gemm_grouped", "fp8q_version", "fp8q_status_string"]:
+    for name in ENTRY_POINTS + ["fp8q_version", "fp8q_status_string"]:
         assert name in syms
 
 
@@ -35,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib()
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert L.fp8q_version() == 100
+    assert L.fp8q_version() == 200
     for s in range(8):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"
@@ -96,6 +100,8 @@ def test_gemm_validation():
     assert f(A, SA + 2, B, SB, C, 0, 64, 128, 128, None) == 3
     assert f(A, SA, B, SB + 2, C, 0, 64, 128, 128, None) == 3
     assert f(A, SA, B, SB, C, 0, 1 << 31, 128, 128, None) == 7
+    assert f(A, SA, B, SB, C, 0, 64, 128, (1 << 23) + 128, None) == 7  # K limit
+    assert f(A, SA, B, SB, C, 0, 64, 128, 1 << 23, None) != 7
     assert f(None, None, None, None, None, 0, 0, 128, 128, None) == 0
     assert f(None, None, None, None, None, 0, 64, 0, 128, None) == 0
 
@@ -114,17 +120,63 @@ def test_grouped_validation():
     assert f(None, None, None, None, None, 1, None, 2, 0, 128, 128, None) == 0
 
 
+@pytest.mark.parametrize("name", ["fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
+                                  "fp8q_transpose_weight_128x128"])
+def test_retile_validation(name):
+    L = _lib()
+    with_scales = name != "fp8q_quant_act_128x1"
+
+    def f(inp, ins, R, C_, out, outs):
+        fn = getattr(L, name)
+        return fn(inp, ins, R, C_, out, outs, None) if with_scales else fn(inp, R, C_, out, outs, None)
+
+    assert f(X, SA, 100, 128, Q, SB) == 2  # rows % 128
+    assert f(X, SA, 128, 100, Q, SB) == 2  # cols % 128
+    assert f(X, SA, -128, 128, Q, SB) == 2
+    assert f(None, SA, 128, 128, Q, SB) == 1
+    assert f(X, SA, 128, 128, None, SB) == 1
+    assert f(X, SA, 128, 128, Q, None) == 1
+    if with_scales:
+        assert f(X, None, 128, 128, Q, SB) == 1
+        assert f(X, SA + 2, 128, 128, Q, SB) == 3
+    assert f(X + 8, SA, 128, 128, Q, SB) == 3
+    assert f(X, SA, 128, 128, Q + 4, SB) == 3
+    assert f(X, SA, 128, 128, Q, SB + 1) == 3
+    assert f(X, SA, 1 << 31, 128, Q, SB) == 7
+    assert f(X, SA, 128, 128 * 65536, Q, SB) == 7
+    assert f(None, None, 0, 128, None, None) == 0
+    assert f(None, None, 128, 0, None, None) == 0
+
+
+def test_rowscaled_gemm_validation():
+    L = _lib()
+    f = L.fp8_gemm_rowscaled
+    assert f(A, SA, B, SB, C, 0, 64, 100, 128, None) == 2
+    assert f(A, SA, B, SB, C, 0, 64, 128, 100, None) == 2
+    assert f(A, SA, B, SB, C, 5, 64, 128, 128, None) == 4
+    for i in range(5):
+        args = [A, SA, B, SB, C]
+        args[i] = None
+        assert f(*args, 0, 64, 128, 128, None) == 1, i
+    assert f(A, SA, B, SB + 2, C, 0, 64, 128, 128, None) == 3
+    assert f(A, SA, B, SB, C, 0, 64, 128, (1 << 23) + 128, None) == 7
+    assert f(None, None, None, None, None, 0, 0, 128, 128, None) == 0
+
+
 @pytest.mark.skipif(gpu_available(), reason="only meaningful without a GPU (fake pointers)")
 def test_valid_call_without_gpu_reports_no_device():
     L = _lib()
     assert L.fp8q_quant_act_1x128(X, 4, 128, Q, SA, None) == 6
     assert L.fp8_gemm_blockscaled(A, SA, B, SB, C, 1, 64, 128, 128, None) == 6
+    assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
+    assert L.fp8q_requant_1x128_to_128x1(X, SA, 128, 128, Q, SB, None) == 6
+    assert L.fp8q_transpose_weight_128x128(X, SA, 128, 128, Q, SB, None) == 6
+    assert L.fp8_gemm_rowscaled(A, SA, B, SB, C, 0, 64, 128, 128, None) == 6
 
 
 def test_binding_names_match_c_abi():
     import fp8_fine_grained_online_amd as pkg
-    for name in ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
-                 "fp8_gemm_grouped"]:
+    for name in ENTRY_POINTS:
         assert callable(getattr(pkg, name))
 
 
