@@ -5,11 +5,14 @@ One step = the whole path over one batch of synthetic inputs already resident
 in HBM: online 1x128 activation quantization, 128x128 weight quantization and
 the block-scaled FP8 GEMM (grouped for the MoE workload). `value` is the GEMM's
 algorithmic FLOPs per step (2*M*N*K; real tokens for MoE) divided by the step
-time, i.e. quantization time is charged to the step. Two timed passes of K
-steps each: the first, with HIP events only at its ends, gives the step time
-and `value`; the second records an event pair around every kernel on the
-launch stream and gives the per-kernel durations (the markers themselves cost
-a few microseconds per kernel, so they are kept out of the first pass).
+time, i.e. quantization time is charged to the step. A backward workload
+(bwd_*) times the layer's Dgrad and Wgrad instead: quantization of dY in 1x128
+and 128x1 tiles (one fused kernel), the weight transpose, re-tiling of the
+stored FP8 X, and the two GEMMs (value = 4*M*N*K per step). Two timed passes of K steps each: the
+first, with HIP events only at its ends, gives the step time and `value`; the
+second records an event pair around every kernel on the launch stream and
+gives the per-kernel durations (the markers themselves cost a few
+microseconds per kernel, so they are kept out of the first pass).
 
 Prints one JSON line. Options: --steps K --warmup W --workload NAME --gpus 1.
 """
@@ -51,15 +54,20 @@ def measured_traffic(workload, kernel_src):
     return rec.get("bytes_per_launch")
 
 
+def oracle_threads():
+    """Threads the oracle's BLAS calls use."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(workload, a_bits, b_bits, rows):
     """The oracle, untuned, on a bounded sample of the same workload."""
     import numpy as np
     from oracle import gemm, quant
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = oracle_threads()
     t0 = time.perf_counter()
     qa, sa = quant.quant_act_1x128(a_bits[:rows])
     qb, sb = quant.quant_weight_128x128(b_bits)
@@ -97,6 +105,151 @@ def copy_calibration(steps, warmup):
     ms = t0.elapsed_time(t1) / steps
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 5),
                       "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
+    """Quantize A and B, then the (grouped) block-scaled GEMM."""
+    import numpy as np
+    import torch
+    grouped = w.G > 0
+    if grouped:
+        a_bits, b_bits, counts, off = S.grouped_inputs(w, args.seed)
+        M, N, K = a_bits.shape[0], w.N, w.K
+        off_d = torch.from_numpy(off).to(dev)
+        flops = 2.0 * w.tokens * N * K
+        b_rows = w.G * N
+    else:
+        a_bits, b_bits = S.dense_inputs(w, args.seed)
+        M, N, K = w.M, w.N, w.K
+        flops = 2.0 * M * N * K
+        b_rows = N
+    A = up_bf16(a_bits)
+    B = up_bf16(b_bits)
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    qb = torch.empty((b_rows, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((b_rows // 128, K // 128), dtype=torch.float32, device=dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    gemm_name = "fp8_gemm_grouped" if grouped else "fp8_gemm_blockscaled"
+    if grouped:
+        gemm = lambda: L.fp8_gemm_grouped(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(),
+                                          C.data_ptr(), F.FP8Q_OUT_BF16, off_d.data_ptr(), w.G, M,
+                                          N, K, sp)
+    else:
+        gemm = lambda: L.fp8_gemm_blockscaled(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(),
+                                              sb.data_ptr(), C.data_ptr(), F.FP8Q_OUT_BF16, M, N,
+                                              K, sp)
+    launches = [
+        ("quant_act_1x128",
+         lambda: L.fp8q_quant_act_1x128(A.data_ptr(), M, K, qa.data_ptr(), sa.data_ptr(), sp)),
+        ("quant_weight_128x128",
+         lambda: L.fp8q_quant_weight_128x128(B.data_ptr(), b_rows, K, qb.data_ptr(), sb.data_ptr(),
+                                             sp)),
+        (gemm_name, gemm),
+    ]
+
+    def cpu():
+        if grouped:
+            r0 = int(off[0])
+            return cpu_baseline(args.workload + " expert 0", a_bits[r0:r0 + 128], b_bits[0], 128)
+        return cpu_baseline(args.workload, a_bits, b_bits, min(M, 1024))
+
+    return {
+        "launches": launches,
+        "flops": {gemm_name: flops},
+        "flops_step": flops,
+        "bytes": {"quant_act_1x128": M * K * 3 + M * (K // 128) * 4,
+                  "quant_weight_128x128": b_rows * K * 3 + (b_rows // 128) * (K // 128) * 4},
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "G": w.G or None,
+                   "tokens": w.tokens or None, "out": "bf16",
+                   "step": "quant_act_1x128 + quant_weight_128x128 + " + gemm_name},
+        "extra": {"gemm_tflops_padded": (gemm_name, 2.0 * M * N * K)},
+        "cpu": cpu,
+    }
+
+
+def plan_backward(w, args, F, S, L, dev, sp, up_bf16):
+    """Dgrad and Wgrad of Y = X W^T (X: M x K, W: N x K, dY: M x N), from the
+    forward's stored FP8 X (1x128) and W (128x128) and the bf16 dY."""
+    import torch
+    M, N, K = w.M, w.N, w.K
+    x_bits, w_bits, dy_bits = S.backward_inputs(w, args.seed)
+    X, W, DY = up_bf16(x_bits), up_bf16(w_bits), up_bf16(dy_bits)
+    u8, f32 = torch.uint8, torch.float32
+    e = lambda *shape, dt=u8: torch.empty(shape, dtype=dt, device=dev)
+    # stored by the forward pass (not part of the timed step)
+    qx, sx = e(M, K), e(M, K // 128, dt=f32)
+    qw, sw = e(N, K), e(N // 128, K // 128, dt=f32)
+    for st in (L.fp8q_quant_act_1x128(X.data_ptr(), M, K, qx.data_ptr(), sx.data_ptr(), sp),
+               L.fp8q_quant_weight_128x128(W.data_ptr(), N, K, qw.data_ptr(), sw.data_ptr(), sp)):
+        if st:
+            raise RuntimeError(f"forward quantization failed with status {st}")
+    qdy, sdy = e(M, N), e(M, N // 128, dt=f32)          # Dgrad A: dY, 1x128
+    qdyt, sdyt = e(N, M), e(N, M // 128, dt=f32)        # Wgrad A: dY^T, 128x1
+    qwt, swt = e(K, N), e(K // 128, N // 128, dt=f32)   # Dgrad B: W^T
+    qxt, sxt = e(K, M), e(K, M // 128, dt=f32)          # Wgrad B: X^T, 128x1
+    dX = e(M, K, dt=torch.bfloat16)
+    dW = e(N, K, dt=f32)
+    launches = [
+        ("quant_act_1x128_128x1",  # dY in both tilings from one read
+         lambda: L.fp8q_quant_act_1x128_128x1(DY.data_ptr(), M, N, qdy.data_ptr(), sdy.data_ptr(),
+                                              qdyt.data_ptr(), sdyt.data_ptr(), sp)),
+        ("transpose_weight_128x128",
+         lambda: L.fp8q_transpose_weight_128x128(qw.data_ptr(), sw.data_ptr(), N, K, qwt.data_ptr(),
+                                                 swt.data_ptr(), sp)),
+        ("requant_1x128_to_128x1",
+         lambda: L.fp8q_requant_1x128_to_128x1(qx.data_ptr(), sx.data_ptr(), M, K, qxt.data_ptr(),
+                                               sxt.data_ptr(), sp)),
+        ("fp8_gemm_blockscaled",   # Dgrad: dX = dY W, reduction over N
+         lambda: L.fp8_gemm_blockscaled(qdy.data_ptr(), sdy.data_ptr(), qwt.data_ptr(),
+                                        swt.data_ptr(), dX.data_ptr(), F.FP8Q_OUT_BF16, M, K, N, sp)),
+        ("fp8_gemm_rowscaled",     # Wgrad: dW = dY^T X, reduction over the M tokens
+         lambda: L.fp8_gemm_rowscaled(qdyt.data_ptr(), sdyt.data_ptr(), qxt.data_ptr(),
+                                      sxt.data_ptr(), dW.data_ptr(), F.FP8Q_OUT_F32, N, K, M, sp)),
+    ]
+    f = 2.0 * M * N * K
+    return {
+        "launches": launches,
+        "flops": {"fp8_gemm_blockscaled": f, "fp8_gemm_rowscaled": f},
+        "flops_step": 2 * f,
+        "bytes": {"quant_act_1x128_128x1": M * N * 4 + 2 * M * (N // 128) * 4,
+                  "transpose_weight_128x128": N * K * 2 + 2 * (N // 128) * (K // 128) * 4,
+                  "requant_1x128_to_128x1": M * K * 2 + 2 * M * (K // 128) * 4},
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "G": None, "tokens": M,
+                   "out": {"dX": "bf16", "dW": "f32"},
+                   "step": "quant_act_1x128_128x1(dY) + Dgrad (transpose_weight_128x128(W) + "
+                           "fp8_gemm_blockscaled) + Wgrad (requant_1x128_to_128x1(X) + "
+                           "fp8_gemm_rowscaled)"},
+        "extra": {},
+        "cpu": lambda: cpu_baseline_backward(args.workload, x_bits, w_bits, dy_bits, 64),
+    }
+
+
+def cpu_baseline_backward(workload, x_bits, w_bits, dy_bits, rows):
+    """The oracle, untuned: `rows` rows of dX and `rows` rows of dW."""
+    import numpy as np
+    from oracle import gemm, quant
+    threads = oracle_threads()
+    M, K = x_bits.shape
+    N = w_bits.shape[0]
+    t0 = time.perf_counter()
+    qd, sd = quant.quant_act_1x128(dy_bits[:rows])
+    qwt, swt = quant.transpose_weight_128x128(*quant.quant_weight_128x128(w_bits))
+    gemm.round_bf16(gemm.gemm_blockscaled_f64(qd, sd, qwt, swt))
+    qdt, sdt = quant.quant_act_1x128(np.ascontiguousarray(dy_bits[:, :rows].T))
+    qxt, sxt = quant.requant_1x128_to_128x1(*quant.quant_act_1x128(x_bits))
+    gemm.round_f32(gemm.gemm_rowscaled_f64(qdt, sdt, qxt, sxt))
+    dt = time.perf_counter() - t0
+    return {
+        "value": (2.0 * rows * K * N + 2.0 * rows * K * M) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{workload}: oracle Dgrad of the first {rows} token rows (1x128 quantization of "
+                   f"dY, weight quantization and transpose, float64 per-group GEMM, bf16) and "
+                   f"Wgrad of the first {rows} output channels (128x1 quantization of dY, "
+                   f"re-tiling of all of X, float64 row-scaled GEMM, float32); {dt:.2f} s"),
+    }
 
 
 def main():
@@ -142,44 +295,18 @@ def main():
     def up_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    grouped = w.G > 0
-    if grouped:
-        a_bits, b_bits, counts, off = S.grouped_inputs(w, args.seed)
-        M, N, K = a_bits.shape[0], w.N, w.K
-        off_d = torch.from_numpy(off).to(dev)
-        flops = 2.0 * w.tokens * N * K
-        flops_padded = 2.0 * M * N * K
-        b_rows = w.G * N
-    else:
-        a_bits, b_bits = S.dense_inputs(w, args.seed)
-        M, N, K = w.M, w.N, w.K
-        flops = flops_padded = 2.0 * M * N * K
-        b_rows = N
-    A = up_bf16(a_bits)
-    B = up_bf16(b_bits)
-    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
-    qb = torch.empty((b_rows, K), dtype=torch.uint8, device=dev)
-    sb = torch.empty((b_rows // 128, K // 128), dtype=torch.float32, device=dev)
-    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    plan = (plan_backward if w.backward else plan_forward)(w, args, F, S, L, dev, sp, up_bf16)
+    launches = plan["launches"]
+    names = [n for n, _ in launches]
 
     def step(ev=None):
+        s = 0
+        for i, (_, fn) in enumerate(launches):
+            if ev:
+                ev[i].record(stream)
+            s |= fn()
         if ev:
-            ev[0].record(stream)
-        s = L.fp8q_quant_act_1x128(A.data_ptr(), M, K, qa.data_ptr(), sa.data_ptr(), sp)
-        if ev:
-            ev[1].record(stream)
-        s |= L.fp8q_quant_weight_128x128(B.data_ptr(), b_rows, K, qb.data_ptr(), sb.data_ptr(), sp)
-        if ev:
-            ev[2].record(stream)
-        if grouped:
-            s |= L.fp8_gemm_grouped(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(),
-                                    C.data_ptr(), F.FP8Q_OUT_BF16, off_d.data_ptr(), w.G, M, N, K, sp)
-        else:
-            s |= L.fp8_gemm_blockscaled(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(),
-                                        C.data_ptr(), F.FP8Q_OUT_BF16, M, N, K, sp)
-        if ev:
-            ev[3].record(stream)
+            ev[len(launches)].record(stream)
         if s:
             raise RuntimeError(f"launch failed with status {s}")
 
@@ -201,25 +328,23 @@ def main():
     ms_step = t_begin.elapsed_time(t_end) / args.steps
 
     # pass 2: per-kernel durations from event pairs on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    q_act = np.mean([e[0].elapsed_time(e[1]) for e in evs])
-    q_w = np.mean([e[1].elapsed_time(e[2]) for e in evs])
-    g_ms = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    kms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
 
-    value = flops / (ms_step * 1e-3) / 1e12
-    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
-    act_bytes = M * K * (2 + 1) + M * (K // 128) * 4
-    w_bytes = b_rows * K * (2 + 1) + (b_rows // 128) * (K // 128) * 4
-    kernel_src = ("gemm.hip", "common.hpp")
-    traffic = measured_traffic(args.workload, kernel_src)
+    # the roofline kernel: the slowest contraction of the step
+    gemm_name = max(plan["flops"], key=lambda n: kms[n])
+    g_ms = kms[gemm_name]
+    gemm_tflops = plan["flops"][gemm_name] / (g_ms * 1e-3) / 1e12
+    traffic = measured_traffic(args.workload, ("gemm.hip", "common.hpp"))
 
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(plan["flops_step"] / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -230,40 +355,26 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8e4m3",
         "data": "synthetic",
-        "config": {
-            "workload": args.workload, "M": M, "N": N, "K": K, "G": w.G or None,
-            "tokens": w.tokens or None, "out": "bf16",
-            "step": "quant_act_1x128 + quant_weight_128x128 + " +
-                    ("fp8_gemm_grouped" if grouped else "fp8_gemm_blockscaled"),
-        },
+        "config": plan["config"],
         "roofline": {
             "bound": "mfma",
-            "kernel": "fp8_gemm_grouped" if grouped else "fp8_gemm_blockscaled",
+            "kernel": gemm_name,
             "achieved": round(gemm_tflops, 2),
             "peak": FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
             "traffic": traffic,
         },
-        "kernels_ms": {
-            "quant_act_1x128": round(q_act, 5),
-            "quant_weight_128x128": round(q_w, 5),
-            "gemm": round(g_ms, 5),
-        },
-        "quant_act_GBps": round(act_bytes / (q_act * 1e-3) / 1e9, 1),
-        "quant_weight_GBps": round(w_bytes / (q_w * 1e-3) / 1e9, 1),
-        "gemm_tflops_padded": round(flops_padded / (g_ms * 1e-3) / 1e12, 2),
+        "kernels_ms": {n: round(v, 5) for n, v in kms.items()},
+        "kernels_GBps": {n: round(b / (kms[n] * 1e-3) / 1e9, 1) for n, b in plan["bytes"].items()},
+        "kernels_TFLOPs": {n: round(f / (kms[n] * 1e-3) / 1e12, 2) for n, f in plan["flops"].items()},
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": None,
     }
+    for key, (n, f) in plan["extra"].items():
+        out[key] = round(f / (kms[n] * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
-        if grouped:
-            e = 0
-            r0 = int(off[e])
-            out["cpu_baseline"] = cpu_baseline(args.workload + f" expert {e}", a_bits[r0:r0 + 128],
-                                               b_bits[e], 128)
-        else:
-            out["cpu_baseline"] = cpu_baseline(args.workload, a_bits, b_bits, min(M, 1024))
+        out["cpu_baseline"] = plan["cpu"]()
     print(json.dumps(out), flush=True)
 
 

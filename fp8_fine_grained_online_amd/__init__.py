@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
   fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype)   -> c
 Backward pass (Dgrad dX = dY W, Wgrad dW = dY^T X):
   fp8q_quant_act_128x1(x)                    -> (qt, st)   128x1 tiles, transposed
+  fp8q_quant_act_1x128_128x1(x)              -> (q, sa, qt, st)   both, one read of x
   fp8q_requant_1x128_to_128x1(q, sa)         -> (qt, st)
   fp8q_transpose_weight_128x128(q, sb)       -> (qt, sbt)
   fp8_gemm_rowscaled(a, sa, b, sb, out_dtype)            -> c
@@ -28,6 +29,7 @@ from ._lib import (  # noqa: F401
     fp8_gemm_grouped,
     fp8_gemm_rowscaled,
     fp8q_quant_act_128x1,
+    fp8q_quant_act_1x128_128x1,
     fp8q_quant_act_1x128,
     fp8q_requant_1x128_to_128x1,
     fp8q_transpose_weight_128x128,
@@ -41,6 +43,6 @@ __all__ = [
     "Fp8qError", "FP8Q_OUT_BF16", "FP8Q_OUT_F32", "STATUS",
     "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
     "fp8_gemm_blockscaled", "fp8_gemm_grouped", "fp8q_version", "lib", "lib_path",
-    "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1", "fp8q_transpose_weight_128x128",
+    "fp8q_quant_act_128x1", "fp8q_quant_act_1x128_128x1", "fp8q_requant_1x128_to_128x1", "fp8q_transpose_weight_128x128",
     "fp8_gemm_rowscaled",
 ]

@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_gemm_grouped.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, vp]
         L.fp8q_quant_act_128x1.restype = i32
         L.fp8q_quant_act_128x1.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fp8q_quant_act_1x128_128x1.restype = i32
+        L.fp8q_quant_act_1x128_128x1.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.fp8q_requant_1x128_to_128x1.restype = i32
         L.fp8q_requant_1x128_to_128x1.argtypes = [vp, vp, i64, i64, vp, vp, vp]
         L.fp8q_transpose_weight_128x128.restype = i32
@@ -213,6 +215,21 @@ def fp8q_quant_act_128x1(x, qt=None, st=None, stream=None):
     _check("fp8q_quant_act_128x1",
            lib().fp8q_quant_act_128x1(px, M, K, qt.data_ptr(), st.data_ptr(), _stream(stream)))
     return qt, st
+
+
+def fp8q_quant_act_1x128_128x1(x, q=None, sa=None, qt=None, st=None, stream=None):
+    """x: bf16 M x K -> (q M x K, sa M x K/128, qt K x M, st K x M/128): both tilings, one read."""
+    torch = _torch()
+    px = _dev(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    q = _out(q, "q", (M, K), torch.uint8, x.device)
+    sa = _out(sa, "sa", (M, _div128(K)), torch.float32, x.device)
+    qt = _out(qt, "qt", (K, M), torch.uint8, x.device)
+    st = _out(st, "st", (K, _div128(M)), torch.float32, x.device)
+    _check("fp8q_quant_act_1x128_128x1",
+           lib().fp8q_quant_act_1x128_128x1(px, M, K, q.data_ptr(), sa.data_ptr(), qt.data_ptr(),
+                                            st.data_ptr(), _stream(stream)))
+    return q, sa, qt, st
 
 
 def fp8q_requant_1x128_to_128x1(q, sa, qt=None, st=None, stream=None):

@@ -26,6 +26,8 @@ hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_
                                  int64_t K, hipStream_t stream);
 hipError_t launch_quant_act_128x1(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
                                   hipStream_t stream);
+hipError_t launch_quant_act_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
+                                 uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_requant_1x128_to_128x1(const uint8_t* q, const float* sa, int64_t M, int64_t K,
                                          uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_transpose_weight_128x128(const uint8_t* q, const float* sb, int64_t N, int64_t K,
@@ -164,6 +166,17 @@ int fp8q_quant_act_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* qt, 
   if (s == -1) return FP8Q_OK;
   if (s || (s = check_device())) return s;
   return launched(fp8q::launch_quant_act_128x1(x_bf16, M, K, qt, st, (hipStream_t)stream));
+}
+
+int fp8q_quant_act_1x128_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,
+                               uint8_t* qt, float* st, void* stream) {
+  int s = check_retile(x_bf16, nullptr, false, M, K, qt, st);
+  if (s == -1) return FP8Q_OK;
+  if (s) return s;
+  if (!q || !sa) return FP8Q_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(sa, 4)) return FP8Q_ERR_ALIGN;
+  if ((s = check_device())) return s;
+  return launched(fp8q::launch_quant_act_dual(x_bf16, M, K, q, sa, qt, st, (hipStream_t)stream));
 }
 
 int fp8q_requant_1x128_to_128x1(const uint8_t* q, const float* sa, int64_t M, int64_t K,

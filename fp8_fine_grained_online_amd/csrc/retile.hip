@@ -12,9 +12,12 @@
 // Of Time" (myomija.com); that the forward activations are kept as 1x128 FP8
 // tiles is in the memory paragraph of the woojincopolymer.co.kr post.
 //
-// One kernel template covers three sources, all mapped 128 x 128 tile by tile
+// One kernel template covers four sources, all mapped 128 x 128 tile by tile
 // from a row-major R x C input to the row-major C x R output:
 //   kBf16      : bf16 activations -> 128x1 quantization (transposed codes)
+//   kBf16Dual  : as kBf16, and also the 1x128 quantization of the same tile
+//                (its 128 rows are whole 1x128 tiles): both layouts of an
+//                output gradient from one read of it
 //   kFp8Scaled : stored 1x128 codes + scales -> each element dequantized to
 //                binary32 (one rounding of code * scale) -> 128x1 quantization
 //   kFp8Copy   : 128x128-block codes copied transposed, block scale moved
@@ -30,17 +33,21 @@
 
 namespace fp8q {
 
-enum class Retile { kBf16, kFp8Scaled, kFp8Copy };
+enum class Retile { kBf16, kBf16Dual, kFp8Scaled, kFp8Copy };
 
 constexpr int kRtThreads = 256;
 constexpr int kRtOutStride = 144;  // LDS bytes per transposed row: 128 codes + 16 pad
 
 template <Retile S>
 struct RetileCfg {
-  static constexpr int kInRowBytes = (S == Retile::kBf16) ? 256 : 128;
-  static constexpr int kInBytes = 128 * kInRowBytes;
+  static constexpr bool kBf16In = (S == Retile::kBf16 || S == Retile::kBf16Dual);
+  static constexpr int kInRowBytes = kBf16In ? 256 : 128;  // one tile row in global memory
+  // LDS row stride: bf16 rows padded by 16 bytes so that the row pass's
+  // 16-byte reads (two threads per row) fall in distinct banks
+  static constexpr int kLdsRow = kBf16In ? 272 : 128;
+  static constexpr int kInBytes = 128 * kLdsRow;
   static constexpr int kBufBytes = kInBytes > 128 * kRtOutStride ? kInBytes : 128 * kRtOutStride;
-  static constexpr int kLoads = kInBytes / 16 / kRtThreads;  // 16-byte chunks per thread
+  static constexpr int kLoads = 128 * kInRowBytes / 16 / kRtThreads;  // 16-byte chunks per thread
 };
 
 // Decode one E4M3 byte (exact in binary32).
@@ -51,11 +58,14 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
 // in:  R x C row-major (bf16 or E4M3 bytes)
 // in_s: kFp8Scaled: R x (C/128) scales; kFp8Copy: (R/128) x (C/128) block scales
 // out: C x R E4M3 bytes;  out_s: kBf16/kFp8Scaled: C x (R/128); kFp8Copy: (C/128) x (R/128)
+// kBf16Dual only: row_q R x C E4M3 bytes and row_s R x (C/128), the 1x128 quantization
 template <Retile S>
 __global__ __launch_bounds__(kRtThreads) void retile_kernel(const uint8_t* __restrict__ in,
                                                             const float* __restrict__ in_s,
                                                             uint8_t* __restrict__ out,
-                                                            float* __restrict__ out_s, int R,
+                                                            float* __restrict__ out_s,
+                                                            uint8_t* __restrict__ row_q,
+                                                            float* __restrict__ row_s, int R,
                                                             int C) {
   using Cfg = RetileCfg<S>;
   __shared__ __attribute__((aligned(16))) uint8_t buf[Cfg::kBufBytes];
@@ -86,10 +96,39 @@ __global__ __launch_bounds__(kRtThreads) void retile_kernel(const uint8_t* __res
 #pragma unroll
     for (int i = 0; i < Cfg::kLoads; ++i) {
       const int c = t + i * kRtThreads;
-      *(uint4*)(buf + c * 16) = v[i];  // row c / kChunksPerRow, chunk c % kChunksPerRow
+      *(uint4*)(buf + (c / kChunksPerRow) * Cfg::kLdsRow + (c % kChunksPerRow) * 16) = v[i];
     }
   }
   __syncthreads();
+
+  // ---- kBf16Dual, row pass: each tile row is one 1x128 tile; thread t
+  // quantizes half t & 1 (64 values) of row t >> 1, the pair exchanging maxima
+  if constexpr (S == Retile::kBf16Dual) {
+    const int row = t >> 1, half = t & 1;
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = *(const uint4*)(buf + row * Cfg::kLdsRow + half * 128 + j * 16);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v[j].x)), fabsf(bf16_hi(v[j].x))),
+                               fmaxf(fabsf(bf16_lo(v[j].y)), fabsf(bf16_hi(v[j].y)))),
+                         fmaxf(fmaxf(fabsf(bf16_lo(v[j].z)), fabsf(bf16_hi(v[j].z))),
+                               fmaxf(fabsf(bf16_lo(v[j].w)), fabsf(bf16_hi(v[j].w))))));
+    // partner lane t ^ 1 (quad_perm [1,0,3,2]); non-negative floats order like their bits
+    const uint32_t mb = __float_as_uint(m);
+    const float amax = __uint_as_float(
+        umax(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, false)));
+    const float s = __fdiv_rn(amax, kFp8Max);
+    const TileDivisor d = make_divisor(s, amax);
+    uint8_t* dst = row_q + ((int64_t)rt * 128 + row) * C + (int64_t)ct * 128 + half * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 lo = quant8(v[2 * j], d), hi = quant8(v[2 * j + 1], d);
+      *(uint4*)(dst + 16 * j) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    if (half == 0) row_s[((int64_t)rt * 128 + row) * Gc + ct] = s;
+  }
 
   // ---- column pass: thread t owns column k, rows 64 h .. 64 h + 63 ----
   const int k = t & 127;
@@ -101,7 +140,7 @@ __global__ __launch_bounds__(kRtThreads) void retile_kernel(const uint8_t* __res
     for (int j = 0; j < 16; ++j) {
       uint32_t d = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) d |= (uint32_t)buf[(64 * h + 4 * j + b) * 128 + k] << (8 * b);
+      for (int b = 0; b < 4; ++b) d |= (uint32_t)buf[(64 * h + 4 * j + b) * Cfg::kLdsRow + k] << (8 * b);
       w[j] = d;
     }
     __syncthreads();  // every read of the input tile is done before it is overwritten
@@ -110,10 +149,10 @@ __global__ __launch_bounds__(kRtThreads) void retile_kernel(const uint8_t* __res
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       const int row = 64 * h + i;
-      if constexpr (S == Retile::kBf16) {
-        v[i] = __uint_as_float((uint32_t)(*(const uint16_t*)(buf + row * 256 + 2 * k)) << 16);
+      if constexpr (Cfg::kBf16In) {
+        v[i] = __uint_as_float((uint32_t)(*(const uint16_t*)(buf + row * Cfg::kLdsRow + 2 * k)) << 16);
       } else {
-        v[i] = __fmul_rn(e4m3_to_f32(buf[row * 128 + k]), row_scale[row]);
+        v[i] = __fmul_rn(e4m3_to_f32(buf[row * Cfg::kLdsRow + k]), row_scale[row]);
       }
     }
     float m = 0.0f;
@@ -155,11 +194,17 @@ __global__ __launch_bounds__(kRtThreads) void retile_kernel(const uint8_t* __res
 
 template <Retile S>
 static hipError_t launch_retile(const void* in, const float* in_s, uint8_t* out, float* out_s,
-                                int64_t R, int64_t C, hipStream_t stream) {
+                                int64_t R, int64_t C, hipStream_t stream,
+                                uint8_t* row_q = nullptr, float* row_s = nullptr) {
   const dim3 grid((unsigned)(R / kGroup), (unsigned)(C / kGroup));
   hipLaunchKernelGGL(retile_kernel<S>, grid, dim3(kRtThreads), 0, stream, (const uint8_t*)in, in_s,
-                     out, out_s, (int)R, (int)C);
+                     out, out_s, row_q, row_s, (int)R, (int)C);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_act_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
+                                 uint8_t* qt, float* st, hipStream_t stream) {
+  return launch_retile<Retile::kBf16Dual>(x, nullptr, qt, st, M, K, stream, q, sa);
 }
 
 hipError_t launch_quant_act_128x1(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,

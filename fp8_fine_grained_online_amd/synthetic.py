@@ -9,6 +9,7 @@ definitions): activations are N(0, 1) with exactly round(0.001 * numel)
 distinct entries, drawn without replacement, multiplied by 100 (outliers, the
 case the pages' fine-grained scaling is meant for); weights are N(0, 0.02).
 Values are drawn in float32 and rounded to bf16 (nearest, ties to even).
+Output gradients dY of the backward workloads are drawn like activations.
 MoE token counts per expert are multinomial(total, uniform), each padded up to a
 multiple of 128 with all-zero rows.
 """
@@ -83,6 +84,7 @@ class Workload:
     out: List[str] = field(default_factory=lambda: ["bf16"])
     G: int = 0  # experts (grouped); 0 = dense
     tokens: int = 0  # grouped: real tokens before padding
+    backward: bool = False  # Dgrad + Wgrad of the layer Y[M x N] = X[M x K] W[N x K]^T
 
 
 WORKLOADS = {
@@ -90,6 +92,8 @@ WORKLOADS = {
     "dense_4096x4096x4096": Workload(1, "dense_4096x4096x4096", 4096, 4096, 4096),
     "proj_8192x7168x2048": Workload(20, "proj_8192x7168x2048", 8192, 7168, 2048),
     "proj_8192x2048x7168": Workload(21, "proj_8192x2048x7168", 8192, 2048, 7168),
+    "bwd_proj_8192x7168x2048": Workload(22, "bwd_proj_8192x7168x2048", 8192, 7168, 2048,
+                                        backward=True),
     "skinny_64x7168x7168": Workload(30, "skinny_64x7168x7168", 64, 7168, 7168),
     "actquant_16384x7168": Workload(31, "actquant_16384x7168", 16384, 0, 7168),
     "moe_g32_65536x4096x7168": Workload(4, "moe_g32_65536x4096x7168", 0, 4096, 7168,
@@ -97,7 +101,7 @@ WORKLOADS = {
 }
 
 # tensor ids inside a workload's seed stream
-T_A, T_B, T_OFFSETS = 0, 1, 2
+T_A, T_B, T_OFFSETS, T_DY = 0, 1, 2, 3
 
 
 def dense_inputs(w: Workload, seed: int = 0, M: Optional[int] = None):
@@ -106,6 +110,13 @@ def dense_inputs(w: Workload, seed: int = 0, M: Optional[int] = None):
     a = activations(M, w.K, rng_for(w.wid, T_A, seed))
     b = weights(w.N, w.K, rng_for(w.wid, T_B, seed)) if w.N else None
     return a, b
+
+
+def backward_inputs(w: Workload, seed: int = 0):
+    """(X bits M x K, W bits N x K, dY bits M x N) for a backward workload."""
+    x, wt = dense_inputs(w, seed)
+    dy = activations(w.M, w.N, rng_for(w.wid, T_DY, seed))
+    return x, wt, dy
 
 
 def grouped_inputs(w: Workload, seed: int = 0):

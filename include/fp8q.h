@@ -167,6 +167,7 @@ FP8Q_API int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* 
  *   Wgrad  dW = dY^T X  : fp8q_quant_act_128x1(dY) and
  *                         fp8q_requant_1x128_to_128x1(stored X) feed
  *                         fp8_gemm_rowscaled (A = dY^T, B = X^T, K = M).
+ *   fp8q_quant_act_1x128_128x1(dY) produces both quantizations of dY at once.
  * ---------------------------------------------------------------------------
  */
 
@@ -189,6 +190,21 @@ FP8Q_API int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* 
  */
 FP8Q_API int fp8q_quant_act_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* qt, float* st,
                                   void* stream);
+
+/*
+ * Both quantizations of one activation (or output-gradient) tensor from a
+ * single read of it: the 1x128 result of fp8q_quant_act_1x128 (q, sa) and
+ * the transposed 128x1 result of fp8q_quant_act_128x1 (qt, st), bit for bit.
+ * Dgrad consumes dY in 1x128 tiles and Wgrad in 128x1 tiles (sources as for
+ * those two calls), so dY is read from memory once instead of twice.
+ *
+ *   x_bf16 : in,  M x K bfloat16, 16-byte aligned
+ *   q, sa  : out, M x K E4M3 (16-byte aligned) and M x (K/128) float32
+ *   qt, st : out, K x M E4M3 (16-byte aligned) and K x (M/128) float32
+ * Requires M % 128 == 0 and K % 128 == 0. M == 0 or K == 0 is a no-op.
+ */
+FP8Q_API int fp8q_quant_act_1x128_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* q,
+                                        float* sa, uint8_t* qt, float* st, void* stream);
 
 /*
  * Re-tiling of stored 1x128 FP8 activations into 128x1 tiles, transposed.

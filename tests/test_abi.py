@@ -26,7 +26,7 @@ def declared_symbols():
 
 ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
                 "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
-                "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled"]
+                "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1"]
 
 
 def test_header_declares_the_entry_points():
@@ -148,6 +148,21 @@ def test_retile_validation(name):
     assert f(None, None, 128, 0, None, None) == 0
 
 
+def test_dual_quant_validation():
+    L = _lib()
+    f = L.fp8q_quant_act_1x128_128x1
+    assert f(X, 100, 128, Q, SA, B, SB, None) == 2
+    assert f(X, 128, 100, Q, SA, B, SB, None) == 2
+    for i in range(5):
+        args = [X, Q, SA, B, SB]
+        args[i] = None
+        assert f(args[0], 128, 128, *args[1:], None) == 1, i
+    assert f(X, 128, 128, Q + 8, SA, B, SB, None) == 3
+    assert f(X, 128, 128, Q, SA + 2, B, SB, None) == 3
+    assert f(X, 128, 128, Q, SA, B + 8, SB, None) == 3
+    assert f(None, 0, 128, None, None, None, None, None) == 0
+
+
 def test_rowscaled_gemm_validation():
     L = _lib()
     f = L.fp8_gemm_rowscaled
@@ -169,6 +184,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert L.fp8q_quant_act_1x128(X, 4, 128, Q, SA, None) == 6
     assert L.fp8_gemm_blockscaled(A, SA, B, SB, C, 1, 64, 128, 128, None) == 6
     assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
+    assert L.fp8q_quant_act_1x128_128x1(X, 128, 128, Q, SA, B, SB, None) == 6
     assert L.fp8q_requant_1x128_to_128x1(X, SA, 128, 128, Q, SB, None) == 6
     assert L.fp8q_transpose_weight_128x128(X, SA, 128, 128, Q, SB, None) == 6
     assert L.fp8_gemm_rowscaled(A, SA, B, SB, C, 0, 64, 128, 128, None) == 6

@@ -1,0 +1,54 @@
+"""bench.py's contract on the CPU: it refuses more than one GPU with a message,
+rejects unknown workloads, and its CPU-baseline legs (the oracle on a bounded
+sample) produce the fields the JSON line carries."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+
+
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = run_bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_unknown_workload_is_rejected():
+    r = run_bench("--workload", "no_such_workload")
+    assert r.returncode == 2 and "unknown" in r.stderr
+
+
+def check_baseline(d):
+    assert d["kind"] == "oracle" and d["unit"] == "TFLOP/s"
+    assert d["value"] > 0 and d["cores"] >= 1 and d["sample"]
+
+
+def test_cpu_baseline_legs_on_tiny_inputs():
+    import bench
+    from fp8_fine_grained_online_amd import synthetic as S
+    a = S.activations(256, 256, S.rng_for(990, 0))
+    b = S.weights(128, 256, S.rng_for(990, 1))
+    check_baseline(bench.cpu_baseline("tiny", a, b, 128))
+    dy = S.activations(256, 128, S.rng_for(990, 2))
+    check_baseline(bench.cpu_baseline_backward("tiny", a, b, dy, 64))
+
+
+def test_backward_workload_inputs_have_the_layer_shapes():
+    from fp8_fine_grained_online_amd import synthetic as S
+    w = S.WORKLOADS["bwd_proj_8192x7168x2048"]
+    assert w.backward and (w.M, w.N, w.K) == (8192, 7168, 2048)
+    small = S.Workload(w.wid, "small", 256, 128, 384, backward=True)
+    x, wt, dy = S.backward_inputs(small)
+    assert x.shape == (256, 384) and wt.shape == (128, 384) and dy.shape == (256, 128)
+    assert x.dtype == wt.dtype == dy.dtype == np.uint16

@@ -95,6 +95,35 @@ def test_128x1_full_size_sampled_columns():
     assert_same(qt[cols], st[cols], want_q, want_s)
 
 
+@pytest.mark.parametrize("M,K", [(128, 128), (256, 384), (1024, 7168)])
+def test_dual_quant_matches_both_tilings(M, K):
+    """One read, both outputs: bit-exact against the 1x128 and 128x1 oracles."""
+    import fp8_fine_grained_online_amd as F
+    from oracle import quant
+    x = S.activations(M, K, S.rng_for(948 + M, K))
+    x[:128, :128] = 0  # a zero 128x128 corner: zero tiles in both tilings
+    q, sa, qt, st = F.fp8q_quant_act_1x128_128x1(to_dev_bf16(x))
+    assert_same(host(q), host(sa), *quant.quant_act_1x128(x))
+    assert_same(host(qt), host(st), *quant.quant_act_128x1(x))
+
+
+def test_dual_quant_exhaustive_rows_and_columns():
+    """The exhaustive table's tiles as rows (1x128) of one 128-row slab and as
+    columns (128x1) of the transposed layout, through the fused kernel."""
+    import fp8_fine_grained_online_amd as F
+    from oracle import quant
+    tiles = S.exhaustive_tiles(127)
+    tiles = tiles[: tiles.shape[0] // 128 * 128]
+    x = np.ascontiguousarray(tiles.reshape(-1, 128, 128).transpose(1, 0, 2).reshape(128, -1))
+    q, sa, qt, st = F.fp8q_quant_act_1x128_128x1(to_dev_bf16(x))
+    assert_same(host(q), host(sa), *quant.quant_act_1x128(x))
+    assert_same(host(qt), host(st), *quant.quant_act_128x1(x))
+    xt = np.ascontiguousarray(tiles.T)  # 128 x T: every tile a column
+    q, sa, qt, st = F.fp8q_quant_act_1x128_128x1(to_dev_bf16(xt))
+    assert_same(host(qt), host(st), *quant.quant_act_1x128(tiles))
+    assert_same(host(q), host(sa), *quant.quant_act_1x128(xt))
+
+
 # ------------------------------------------------------------------- requant
 
 @pytest.mark.parametrize("M,K", [(128, 128), (256, 384), (512, 2048)])
@@ -292,7 +321,7 @@ def test_wgrad_full_size_sampled():
     T, N, K = 8192, 7168, 2048
     dy = S.activations(T, N, S.rng_for(962, 0))
     x = S.activations(T, K, S.rng_for(962, 1))
-    qdt, sdt = F.fp8q_quant_act_128x1(to_dev_bf16(dy))
+    _, _, qdt, sdt = F.fp8q_quant_act_1x128_128x1(to_dev_bf16(dy))
     qx, sx = F.fp8q_quant_act_1x128(to_dev_bf16(x))
     qxt, sxt = F.fp8q_requant_1x128_to_128x1(qx, sx)
     dw = poisoned((N, K), torch.float32)
