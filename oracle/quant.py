@@ -98,9 +98,10 @@ def _quant_rows_f32(x32: np.ndarray):
 def requant_1x128_to_128x1(codes: np.ndarray, scales: np.ndarray):
     """Stored 1x128 FP8 activations -> 128x1 tiles, transposed (K x M codes).
 
-    The pages store the forward activations as 1x128 FP8 tiles and convert
-    them to 128x1 tiles for the backward pass ("Six Reasons Deepseek Ai Is A
-    Waste Of Time": the memory paragraph and the sentence next to Figure 7 (a)).
+    The pages store the forward activations as 1x128 FP8 tiles (woojincopolymer.co.kr
+    post, memory paragraph; "Six Reasons Deepseek Ai Is A Waste Of Time" on
+    compressing cached activations) and convert them to 128x1 tiles for the
+    backward pass (the sentence next to the Figure 7 (a) passage of the latter).
     Reading: each element is dequantized to binary32, v = fl32(dec(q) * s)
     (one rounding of the exact product), and v^T is quantized in 1x128 tiles
     with the usual rule.
