@@ -37,6 +37,7 @@ Modules:
   quant    1x128 activation and 128x128 weight quantization.
   gemm     block-scaled GEMM (dense, grouped) as exact per-group float64 sums.
   accsim   limited-precision accumulator model for the K = 4096 demonstration.
+  norm     RMS / layer normalization whose binary32 output feeds the 1x128 cast.
 """
 
 from . import e4m3, bf16, quant, gemm, accsim  # noqa: F401
