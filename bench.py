@@ -14,6 +14,9 @@ second records an event pair around every kernel on the launch stream and
 gives the per-kernel durations (the markers themselves cost a few
 microseconds per kernel, so they are kept out of the first pass).
 
+Stream workloads (actquant_*, normquant_*) time one HBM-bound kernel and report
+GB/s of algorithmic traffic against the 8 TB/s HBM peak.
+
 Prints one JSON line. Options: --steps K --warmup W --workload NAME --gpus 1.
 """
 
@@ -30,6 +33,9 @@ sys.path.insert(0, ROOT)
 METRIC = "block-scaled FP8 GEMM TFLOPS & % of FP8 MFMA peak (4096^3, grouped MoE)"
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+# sources whose hash keys the recorded counters of each streaming kernel
+STREAM_SOURCES = {"quant_act_1x128": ("quant.hip", "common.hpp"),
+                  "norm_quant_act_1x128": ("norm.hip", "common.hpp")}
 
 
 def source_hash(*names):
@@ -225,6 +231,63 @@ def plan_backward(w, args, F, S, L, dev, sp, up_bf16):
     }
 
 
+def plan_stream(w, args, F, S, L, dev, sp, up_bf16):
+    """HBM-streaming workloads: standalone 1x128 quantization, or RMS
+    normalization fused with it; value in GB/s of algorithmic traffic."""
+    import torch
+    from fp8_fine_grained_online_amd.synthetic import T_B
+    M, K = w.M, w.K
+    x_bits, _ = S.dense_inputs(w, args.seed)
+    X = up_bf16(x_bits)
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    nbytes = M * K * 3 + M * (K // 128) * 4
+    if w.name.startswith("normquant"):
+        g_bits, _ = S.norm_params(K, S.rng_for(w.wid, T_B, args.seed))
+        g = up_bf16(g_bits)
+        name = "norm_quant_act_1x128"
+        fn = lambda: L.fp8q_norm_quant_act_1x128(X.data_ptr(), g.data_ptr(), None, 1e-6, 0, M, K,
+                                                 q.data_ptr(), sa.data_ptr(), sp)
+        nbytes += 2 * K
+        cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, 256, g_bits)
+    else:
+        name = "quant_act_1x128"
+        fn = lambda: L.fp8q_quant_act_1x128(X.data_ptr(), M, K, q.data_ptr(), sa.data_ptr(), sp)
+        cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, 2048, None)
+    return {
+        "launches": [(name, fn)],
+        "flops": {},
+        "bytes": {name: nbytes},
+        "stream": name,
+        "config": {"workload": args.workload, "M": M, "K": K,
+                   "step": name + (" (RMS, eps 1e-6)" if name.startswith("norm") else ""),
+                   "bytes_per_step": nbytes},
+        "extra": {},
+        "cpu": cpu,
+    }
+
+
+def cpu_baseline_stream(workload, x_bits, bytes_per_row, rows, gamma_bits):
+    """The oracle, untuned, on the first `rows` rows."""
+    from oracle import norm, quant
+    threads = oracle_threads()
+    t0 = time.perf_counter()
+    if gamma_bits is None:
+        quant.quant_act_1x128(x_bits[:rows])
+        what = "1x128 quantization"
+    else:
+        norm.norm_quant_act_1x128(x_bits[:rows], gamma_bits, 1e-6)
+        what = "RMS normalization + 1x128 quantization"
+    dt = time.perf_counter() - t0
+    return {
+        "value": bytes_per_row * rows / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{workload}: oracle {what} of the first {rows} rows; {dt:.2f} s",
+    }
+
+
 def cpu_baseline_backward(workload, x_bits, w_bits, dy_bits, rows):
     """The oracle, untuned: `rows` rows of dX and `rows` rows of dW."""
     import numpy as np
@@ -281,9 +344,9 @@ def main():
     import fp8_fine_grained_online_amd as F
     from fp8_fine_grained_online_amd import synthetic as S
 
-    if args.workload not in S.WORKLOADS or args.workload == "actquant_16384x7168":
-        print(f"unknown GEMM workload {args.workload}; choose from "
-              f"{[k for k in S.WORKLOADS if not k.startswith('actquant')]}", file=sys.stderr)
+    if args.workload not in S.WORKLOADS:
+        print(f"unknown workload {args.workload}; choose from {list(S.WORKLOADS)}",
+              file=sys.stderr)
         sys.exit(2)
     w = S.WORKLOADS[args.workload]
     L = F.lib()
@@ -295,7 +358,8 @@ def main():
     def up_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    plan = (plan_backward if w.backward else plan_forward)(w, args, F, S, L, dev, sp, up_bf16)
+    kind = plan_backward if w.backward else (plan_stream if w.N == 0 else plan_forward)
+    plan = kind(w, args, F, S, L, dev, sp, up_bf16)
     launches = plan["launches"]
     names = [n for n, _ in launches]
 
@@ -336,16 +400,30 @@ def main():
     torch.cuda.synchronize()
     kms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
 
-    # the roofline kernel: the slowest contraction of the step
-    gemm_name = max(plan["flops"], key=lambda n: kms[n])
-    g_ms = kms[gemm_name]
-    gemm_tflops = plan["flops"][gemm_name] / (g_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload, ("gemm.hip", "common.hpp"))
+    if "stream" in plan:
+        # HBM-bound workload: GB/s of algorithmic traffic against the HBM peak
+        name = plan["stream"]
+        gbps = plan["bytes"][name] / (kms[name] * 1e-3) / 1e9
+        metric = f"{name} HBM GB/s & % of HBM peak"
+        value, unit = plan["bytes"][name] / (ms_step * 1e-3) / 1e9, "GB/s"
+        roofline = {"bound": "hbm", "kernel": name, "achieved": round(gbps, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(args.workload, STREAM_SOURCES[name])}
+    else:
+        # the roofline kernel: the slowest contraction of the step
+        gemm_name = max(plan["flops"], key=lambda n: kms[n])
+        gemm_tflops = plan["flops"][gemm_name] / (kms[gemm_name] * 1e-3) / 1e12
+        metric = METRIC
+        value, unit = plan["flops_step"] / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+        roofline = {"bound": "mfma", "kernel": gemm_name, "achieved": round(gemm_tflops, 2),
+                    "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(args.workload, ("gemm.hip", "common.hpp"))}
 
     out = {
-        "metric": METRIC,
-        "value": round(plan["flops_step"] / (ms_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -356,15 +434,7 @@ def main():
         "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": plan["config"],
-        "roofline": {
-            "bound": "mfma",
-            "kernel": gemm_name,
-            "achieved": round(gemm_tflops, 2),
-            "peak": FP8_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-        },
+        "roofline": roofline,
         "kernels_ms": {n: round(v, 5) for n, v in kms.items()},
         "kernels_GBps": {n: round(b / (kms[n] * 1e-3) / 1e9, 1) for n, b in plan["bytes"].items()},
         "kernels_TFLOPs": {n: round(f / (kms[n] * 1e-3) / 1e12, 2) for n, f in plan["flops"].items()},

@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_gemm_grouped.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, vp]
         L.fp8q_quant_act_128x1.restype = i32
         L.fp8q_quant_act_128x1.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fp8q_norm_quant_act_1x128.restype = i32
+        L.fp8q_norm_quant_act_1x128.argtypes = [vp, vp, vp, ctypes.c_float, i32, i64, i64, vp, vp, vp]
         L.fp8q_quant_act_1x128_128x1.restype = i32
         L.fp8q_quant_act_1x128_128x1.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         L.fp8q_requant_1x128_to_128x1.restype = i32
@@ -215,6 +217,25 @@ def fp8q_quant_act_128x1(x, qt=None, st=None, stream=None):
     _check("fp8q_quant_act_128x1",
            lib().fp8q_quant_act_128x1(px, M, K, qt.data_ptr(), st.data_ptr(), _stream(stream)))
     return qt, st
+
+
+def fp8q_norm_quant_act_1x128(x, gamma, eps, beta=None, centred=False, q=None, sa=None,
+                              stream=None):
+    """Normalize rows of x (bf16 M x K; RMS, or centred with beta) and quantize the
+    binary32 result per 1x128 tile -> (q uint8 M x K, sa float32 M x K/128)."""
+    torch = _torch()
+    px = _dev(x, "x", torch.bfloat16, 2)
+    pg = _dev(gamma, "gamma", torch.bfloat16, 1)
+    pb = _dev(beta, "beta", torch.bfloat16, 1) if beta is not None else None
+    M, K = x.shape
+    if gamma.shape[0] != K or (beta is not None and beta.shape[0] != K):
+        raise ValueError("gamma and beta must have K entries")
+    q = _out(q, "q", (M, K), torch.uint8, x.device)
+    sa = _out(sa, "sa", (M, _div128(K)), torch.float32, x.device)
+    _check("fp8q_norm_quant_act_1x128",
+           lib().fp8q_norm_quant_act_1x128(px, pg, pb, float(eps), int(bool(centred)), M, K,
+                                           q.data_ptr(), sa.data_ptr(), _stream(stream)))
+    return q, sa
 
 
 def fp8q_quant_act_1x128_128x1(x, q=None, sa=None, qt=None, st=None, stream=None):

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfp8q.so")
 
-SOURCES = ["quant.hip", "retile.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "retile.hip", "norm.hip", "gemm.hip", "api.cpp"]
 HEADERS = ["common.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,6 +23,11 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
     # packed-FP32 VALU forms are disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit multiply-add fusion: every rounding the kernels' arithmetic
+    # is specified with happens as written (HIP's header versions of the
+    # __fmul_rn/__dmul_rn intrinsics are plain products that would otherwise
+    # be contracted into a following addition); FMAs are always explicit
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]

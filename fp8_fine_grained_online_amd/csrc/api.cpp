@@ -26,6 +26,9 @@ hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_
                                  int64_t K, hipStream_t stream);
 hipError_t launch_quant_act_128x1(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
                                   hipStream_t stream);
+hipError_t launch_norm_quant_act_1x128(const void* x, const void* gamma, const void* beta,
+                                       float eps, bool centred, int64_t M, int64_t K, uint8_t* q,
+                                       float* sa, hipStream_t stream);
 hipError_t launch_quant_act_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
                                  uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_requant_1x128_to_128x1(const uint8_t* q, const float* sa, int64_t M, int64_t K,
@@ -41,6 +44,8 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;  // kernels index rows/cols 
 // GEMM operand tiles (up to 256 rows of K bytes) are addressed with 32-bit
 // offsets through buffer descriptors
 constexpr int64_t kMaxK = int64_t(1) << 23;
+// the fused normalization keeps a row in one wavefront's registers
+constexpr int64_t kNormMaxK = 16384;
 constexpr int kMaxDevices = 64;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -166,6 +171,24 @@ int fp8q_quant_act_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* qt, 
   if (s == -1) return FP8Q_OK;
   if (s || (s = check_device())) return s;
   return launched(fp8q::launch_quant_act_128x1(x_bf16, M, K, qt, st, (hipStream_t)stream));
+}
+
+int fp8q_norm_quant_act_1x128(const void* x_bf16, const void* gamma_bf16, const void* beta_bf16,
+                              float eps, int centred, int64_t M, int64_t K, uint8_t* q, float* sa,
+                              void* stream) {
+  if (M < 0 || K < 0 || K % kGroup) return FP8Q_ERR_SHAPE;
+  if (centred != 0 && centred != 1) return FP8Q_ERR_SHAPE;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return FP8Q_ERR_SHAPE;  // NaN, negative or infinite
+  if (M > kMaxDim || K > kNormMaxK) return FP8Q_ERR_TOO_LARGE;
+  if (M == 0 || K == 0) return FP8Q_OK;
+  if (!x_bf16 || !gamma_bf16 || !q || !sa || (centred && !beta_bf16)) return FP8Q_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(gamma_bf16, 16) || !aligned(q, 16) || !aligned(sa, 4))
+    return FP8Q_ERR_ALIGN;
+  if (centred && !aligned(beta_bf16, 16)) return FP8Q_ERR_ALIGN;
+  if (int s = check_device()) return s;
+  return launched(fp8q::launch_norm_quant_act_1x128(x_bf16, gamma_bf16, beta_bf16, eps,
+                                                    centred == 1, M, K, q, sa,
+                                                    (hipStream_t)stream));
 }
 
 int fp8q_quant_act_1x128_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,

@@ -1,0 +1,219 @@
+// Layer normalization fused with the 1x128 FP8 cast, for gfx950.
+//
+// The woojincopolymer.co.kr post (hardware suggestions) wants layer
+// normalization and the FP8 cast fused; "Six Reasons Deepseek Ai Is A Waste Of
+// Time" keeps normalization in higher precision while the GEMMs run in FP8.
+// Here one wavefront normalizes one row held in its registers (eight rows per
+// workgroup share gamma and beta, staged once in LDS) and quantizes
+// the binary32 result per 1x128 tile straight to E4M3 codes and scales: the
+// row is read from HBM once and no BF16 copy of the normalized row exists.
+//
+// Per row x (K bf16 values):
+//   RMS:      S = sum x^2,  r = fl32(1 / sqrt(S/K + eps)),  y = fl32(fl32(x r) g)
+//   centred:  mu = sum x / K,  var = sum fl64(x - mu)^2 / K,
+//             r = fl32(1 / sqrt(var + eps)),
+//             y = fl32(fl32(fl32(fl32(x - fl32(mu)) r) g) + b)
+// with every float64 step correctly rounded (division, square root) and the
+// sums formed as double-double (error-free TwoSum per term, then a butterfly
+// across the wavefront whose every combination is symmetric, so all lanes hold
+// the same bits): the statistics are the correctly rounded exact sums, not a
+// function of the summation order. Then y is quantized per 1x128 tile with the
+// activation rule (amax, s = fl32(amax/448), codes of fl32(y/s)).
+//
+// Every rounding above must happen as written: the library is compiled with
+// floating-point contraction off, so no product is fused into the addition
+// that follows it (e.g. the "+ b" or the sum of d * d).
+#include "common.hpp"
+
+namespace fp8q {
+
+constexpr int kNormThreads = 512;  // 8 rows per workgroup, one per wavefront
+
+struct DD {
+  double hi, lo;
+};
+
+// Knuth's TwoSum: s + e == a + b exactly
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = __dadd_rn(a, b);
+  const double bb = __dsub_rn(s, a);
+  e = __dadd_rn(__dsub_rn(a, __dsub_rn(s, bb)), __dsub_rn(b, bb));
+}
+
+__device__ __forceinline__ DD dd_add_term(DD acc, double p) {
+  double s, e;
+  two_sum(acc.hi, p, s, e);
+  return DD{s, __dadd_rn(acc.lo, e)};
+}
+
+// (a.hi + a.lo) + (b.hi + b.lo), renormalized; symmetric in a and b
+__device__ __forceinline__ DD dd_add(DD a, DD b) {
+  double s, e;
+  two_sum(a.hi, b.hi, s, e);
+  e = __dadd_rn(e, __dadd_rn(a.lo, b.lo));
+  const double hi = __dadd_rn(s, e);
+  return DD{hi, __dsub_rn(e, __dsub_rn(hi, s))};
+}
+
+__device__ __forceinline__ double wave_sum(DD v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    DD o;
+    o.hi = __shfl_xor(v.hi, m);
+    o.lo = __shfl_xor(v.lo, m);
+    v = dd_add(v, o);
+  }
+  return __dadd_rn(v.hi, v.lo);
+}
+
+__device__ __forceinline__ float inv_std(double stat_over_k, float eps) {
+  const double t = __dadd_rn(stat_over_k, (double)eps);
+  return (float)__ddiv_rn(1.0, __dsqrt_rn(t));
+}
+
+// An empty asm that "modifies" the packed row: values unpacked from it before
+// cannot be reused after, so each pass re-unpacks (a few bit operations)
+// instead of keeping 8 floats or doubles per chunk live across passes.
+template <int N>
+__device__ __forceinline__ void reunpack_fence(uint4 (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+}
+
+__device__ __forceinline__ void unpack8(uint4 w, float f[8]) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+// kChunks: the most 16-byte chunks (8 values) a lane holds, K <= kChunks * 512
+template <int kChunks, bool kCentred>
+__global__ __launch_bounds__(kNormThreads) void norm_quant_1x128_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
+    float eps, uint2* __restrict__ q, float* __restrict__ sa, int M, int K) {
+  // gamma (and beta) for all rows of the workgroup, staged once in LDS
+  extern __shared__ uint4 params[];  // [K/8] gamma, then [K/8] beta when centred
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kNormThreads / 64) + (threadIdx.x >> 6);
+  const bool active = row < M;  // whole wavefront
+  const int n_chunks = K / 8;
+  const uint4* xr = x + (int64_t)row * n_chunks;
+
+  // chunk lane + 64 i of the row; a 1x128 tile is 16 chunks = one DPP row of
+  // 16 lanes within one i. The row's loads are issued first.
+  uint4 v[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = (active && c < n_chunks) ? load_nt(xr + c) : make_uint4(0, 0, 0, 0);  // absent: zeros
+  }
+  for (int c = threadIdx.x; c < n_chunks; c += kNormThreads) {
+    params[c] = gamma[c];
+    if constexpr (kCentred) params[n_chunks + c] = beta[c];
+  }
+  __syncthreads();
+  if (!active) return;
+
+  float r, mu32 = 0.0f;
+  if constexpr (kCentred) {
+    DD s1{0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      float f[8];
+      unpack8(v[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s1 = dd_add_term(s1, (double)f[e]);
+    }
+    const double mu = __ddiv_rn(wave_sum(s1), (double)K);
+    reunpack_fence(v);
+    DD s2{0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      if (lane + 64 * i >= n_chunks) continue;  // absent chunks would add mu^2
+      float f[8];
+      unpack8(v[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double d = __dsub_rn((double)f[e], mu);
+        s2 = dd_add_term(s2, __dmul_rn(d, d));
+      }
+    }
+    r = inv_std(__ddiv_rn(wave_sum(s2), (double)K), eps);
+    mu32 = (float)mu;
+  } else {
+    DD s2{0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      float f[8];
+      unpack8(v[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s2 = dd_add_term(s2, __dmul_rn((double)f[e], (double)f[e]));
+    }
+    r = inv_std(__ddiv_rn(wave_sum(s2), (double)K), eps);
+  }
+
+  reunpack_fence(v);
+  const int G = K / kGroup;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (64 * i >= n_chunks) break;  // uniform: no chunk of this i exists
+    const bool have = c < n_chunks;  // whole DPP rows (tiles) are present or absent
+    float f[8], g[8], b[8];
+    unpack8(v[i], f);
+    unpack8(have ? params[c] : make_uint4(0, 0, 0, 0), g);
+    if constexpr (kCentred) unpack8(have ? params[n_chunks + c] : make_uint4(0, 0, 0, 0), b);
+    float y[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (kCentred)
+        y[e] = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(f[e], mu32), r), g[e]), b[e]);
+      else
+        y[e] = __fmul_rn(__fmul_rn(f[e], r), g[e]);
+      m = fmaxf(m, fabsf(y[e]));
+    }
+    const float amax = __uint_as_float(row16_max_u32(__float_as_uint(m)));
+    const float s = __fdiv_rn(amax, kFp8Max);
+    const TileDivisor d = make_divisor(s, amax);
+    uint2 out;
+    out.x = pack4_e4m3(quotient(y[0], d), quotient(y[1], d), quotient(y[2], d), quotient(y[3], d));
+    out.y = pack4_e4m3(quotient(y[4], d), quotient(y[5], d), quotient(y[6], d), quotient(y[7], d));
+    if (have) {
+      q[(int64_t)row * n_chunks + c] = out;
+      if ((lane & 15) == 0) sa[(int64_t)row * G + (c >> 4)] = s;
+    }
+  }
+}
+
+template <int kChunks>
+static hipError_t launch_norm_chunks(const void* x, const void* gamma, const void* beta, float eps,
+                                     bool centred, int64_t M, int64_t K, uint8_t* q, float* sa,
+                                     hipStream_t stream) {
+  const int rows = kNormThreads / 64;
+  const dim3 grid((unsigned)((M + rows - 1) / rows));
+  const size_t lds = (size_t)(centred ? 2 : 1) * (size_t)K * 2;  // gamma (+ beta), bf16
+  if (centred)
+    hipLaunchKernelGGL((norm_quant_1x128_kernel<kChunks, true>), grid, dim3(kNormThreads), lds,
+                       stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta, eps,
+                       (uint2*)q, sa, (int)M, (int)K);
+  else
+    hipLaunchKernelGGL((norm_quant_1x128_kernel<kChunks, false>), grid, dim3(kNormThreads), lds,
+                       stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta, eps,
+                       (uint2*)q, sa, (int)M, (int)K);
+  return hipGetLastError();
+}
+
+constexpr int64_t kNormMaxK = 16384;
+
+hipError_t launch_norm_quant_act_1x128(const void* x, const void* gamma, const void* beta,
+                                       float eps, bool centred, int64_t M, int64_t K, uint8_t* q,
+                                       float* sa, hipStream_t stream) {
+  const int64_t per_lane = (K / 8 + 63) / 64;  // chunks per lane
+  if (per_lane <= 2) return launch_norm_chunks<2>(x, gamma, beta, eps, centred, M, K, q, sa, stream);
+  if (per_lane <= 4) return launch_norm_chunks<4>(x, gamma, beta, eps, centred, M, K, q, sa, stream);
+  if (per_lane <= 8) return launch_norm_chunks<8>(x, gamma, beta, eps, centred, M, K, q, sa, stream);
+  if (per_lane <= 16) return launch_norm_chunks<16>(x, gamma, beta, eps, centred, M, K, q, sa, stream);
+  return launch_norm_chunks<32>(x, gamma, beta, eps, centred, M, K, q, sa, stream);
+}
+
+}  // namespace fp8q

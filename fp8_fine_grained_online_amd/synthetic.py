@@ -9,7 +9,8 @@ definitions): activations are N(0, 1) with exactly round(0.001 * numel)
 distinct entries, drawn without replacement, multiplied by 100 (outliers, the
 case the pages' fine-grained scaling is meant for); weights are N(0, 0.02).
 Values are drawn in float32 and rounded to bf16 (nearest, ties to even).
-Output gradients dY of the backward workloads are drawn like activations.
+Output gradients dY of the backward workloads are drawn like activations;
+normalization scales are 1 + N(0, 0.1) and shifts N(0, 0.05).
 MoE token counts per expert are multinomial(total, uniform), each padded up to a
 multiple of 128 with all-zero rows.
 """
@@ -96,6 +97,7 @@ WORKLOADS = {
                                         backward=True),
     "skinny_64x7168x7168": Workload(30, "skinny_64x7168x7168", 64, 7168, 7168),
     "actquant_16384x7168": Workload(31, "actquant_16384x7168", 16384, 0, 7168),
+    "normquant_16384x7168": Workload(32, "normquant_16384x7168", 16384, 0, 7168),
     "moe_g32_65536x4096x7168": Workload(4, "moe_g32_65536x4096x7168", 0, 4096, 7168,
                                         G=32, tokens=65536),
 }
@@ -110,6 +112,13 @@ def dense_inputs(w: Workload, seed: int = 0, M: Optional[int] = None):
     a = activations(M, w.K, rng_for(w.wid, T_A, seed))
     b = weights(w.N, w.K, rng_for(w.wid, T_B, seed)) if w.N else None
     return a, b
+
+
+def norm_params(K: int, rng: np.random.Generator):
+    """(gamma, beta) bf16 bits of a normalization layer: 1 + N(0, 0.1), N(0, 0.05)."""
+    g = f32_to_bf16_bits(1.0 + 0.1 * rng.standard_normal(K, dtype=np.float32))
+    b = f32_to_bf16_bits(0.05 * rng.standard_normal(K, dtype=np.float32))
+    return g, b
 
 
 def backward_inputs(w: Workload, seed: int = 0):

@@ -153,6 +153,37 @@ FP8Q_API int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* 
                      int64_t M_total, int64_t N, int64_t K, void* stream);
 
 /*
+ * Layer normalization fused with the 1x128 activation quantization.
+ * Source: the woojincopolymer.co.kr post, paragraph of hardware suggestions
+ * (a warp-level cast to fuse layer normalization with the FP8 cast), and
+ * "Six Reasons Deepseek Ai Is A Waste Of Time" (normalization kept in higher
+ * precision while the GEMMs run in FP8).
+ *
+ * Per row x (K values), with statistics from exact sums rounded once to
+ * float64 and every float64 step correctly rounded:
+ *   centred = 0 (RMS):   r = fl32(1 / sqrt(fl64(sum x^2 / K) + eps)),
+ *                        y = fl32(fl32(x * r) * gamma)
+ *   centred = 1 (layer): mu = fl64(sum x / K),
+ *                        var = fl64(sum fl64(fl64(x - mu)^2) / K),
+ *                        r = fl32(1 / sqrt(var + eps)),
+ *                        y = fl32(fl32(fl32(fl32(x - fl32(mu)) * r) * gamma) + beta)
+ * then y (binary32, never stored) is quantized per 1x128 tile exactly like
+ * fp8q_quant_act_1x128 quantizes its input.
+ *
+ *   x_bf16     : in,  M x K bfloat16, 16-byte aligned
+ *   gamma_bf16 : in,  K bfloat16 scale, 16-byte aligned
+ *   beta_bf16  : in,  K bfloat16 shift (centred = 1 only; may be NULL otherwise)
+ *   eps        : finite, >= 0 (a zero row with eps = 0 gives non-finite values,
+ *                outside the contract)
+ *   q, sa      : out, M x K E4M3 (16-byte aligned), M x (K/128) float32
+ * Requires K % 128 == 0 and K <= 16384 (a row lives in one wavefront's
+ * registers). M == 0 or K == 0 is a no-op.
+ */
+FP8Q_API int fp8q_norm_quant_act_1x128(const void* x_bf16, const void* gamma_bf16,
+                                       const void* beta_bf16, float eps, int centred, int64_t M,
+                                       int64_t K, uint8_t* q, float* sa, void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * Backward pass of a linear layer Y = X W^T (X: M tokens x K in-channels,
  * W: N out-channels x K). "Six Reasons Deepseek Ai Is A Waste Of Time": the

@@ -26,7 +26,8 @@ def declared_symbols():
 
 ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
                 "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
-                "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1"]
+                "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1",
+                "fp8q_norm_quant_act_1x128"]
 
 
 def test_header_declares_the_entry_points():
@@ -163,6 +164,29 @@ def test_dual_quant_validation():
     assert f(None, 0, 128, None, None, None, None, None) == 0
 
 
+def test_norm_quant_validation():
+    L = _lib()
+    f = L.fp8q_norm_quant_act_1x128
+    G_, BETA = B, SB  # fake gamma / beta addresses (16-byte aligned)
+    assert f(X, G_, BETA, 1e-6, 0, 4, 100, Q, SA, None) == 2           # K % 128
+    assert f(X, G_, BETA, 1e-6, 0, -1, 128, Q, SA, None) == 2
+    assert f(X, G_, BETA, 1e-6, 2, 4, 128, Q, SA, None) == 2           # centred flag
+    assert f(X, G_, BETA, -1.0, 0, 4, 128, Q, SA, None) == 2           # eps < 0
+    assert f(X, G_, BETA, float("nan"), 0, 4, 128, Q, SA, None) == 2
+    assert f(X, G_, BETA, float("inf"), 0, 4, 128, Q, SA, None) == 2
+    assert f(X, G_, BETA, 1e-6, 0, 4, 16384 + 128, Q, SA, None) == 7  # row must fit a wavefront
+    assert f(None, G_, BETA, 1e-6, 0, 4, 128, Q, SA, None) == 1
+    assert f(X, None, BETA, 1e-6, 0, 4, 128, Q, SA, None) == 1
+    assert f(X, G_, None, 1e-6, 1, 4, 128, Q, SA, None) == 1          # centred needs beta
+    assert f(X, G_, BETA, 1e-6, 0, 4, 128, None, SA, None) == 1
+    assert f(X, G_, BETA, 1e-6, 0, 4, 128, Q, None, None) == 1
+    assert f(X, G_ + 4, BETA, 1e-6, 0, 4, 128, Q, SA, None) == 3
+    assert f(X, G_, BETA + 4, 1e-6, 1, 4, 128, Q, SA, None) == 3
+    assert f(X + 2, G_, BETA, 1e-6, 0, 4, 128, Q, SA, None) == 3
+    assert f(X, G_, BETA, 1e-6, 0, 4, 128, Q, SA + 1, None) == 3
+    assert f(None, None, None, 1e-6, 0, 0, 128, None, None, None) == 0
+
+
 def test_rowscaled_gemm_validation():
     L = _lib()
     f = L.fp8_gemm_rowscaled
@@ -185,6 +209,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert L.fp8_gemm_blockscaled(A, SA, B, SB, C, 1, 64, 128, 128, None) == 6
     assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
     assert L.fp8q_quant_act_1x128_128x1(X, 128, 128, Q, SA, B, SB, None) == 6
+    assert L.fp8q_norm_quant_act_1x128(X, B, None, 1e-6, 0, 4, 128, Q, SA, None) == 6
     assert L.fp8q_requant_1x128_to_128x1(X, SA, 128, 128, Q, SB, None) == 6
     assert L.fp8q_transpose_weight_128x128(X, SA, 128, 128, Q, SB, None) == 6
     assert L.fp8_gemm_rowscaled(A, SA, B, SB, C, 0, 64, 128, 128, None) == 6
@@ -209,3 +234,12 @@ def test_oracle_and_hip_path_share_no_code():
         if fn.endswith(".py"):
             text = open(os.path.join(ROOT, "oracle", fn)).read()
             assert "fp8_fine_grained_online_amd" not in text, fn
+
+
+def test_device_code_is_built_without_contraction_or_packed_fp32():
+    """The kernels' roundings must happen as written (parity is bit-exact for
+    codes), and packed FP32 VALU forms stay disabled."""
+    from fp8_fine_grained_online_amd import build
+    assert "-ffp-contract=off" in build.FLAGS
+    i = build.FLAGS.index("-packed-fp32-ops")
+    assert build.FLAGS[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
