@@ -38,6 +38,7 @@ Modules:
   gemm     block-scaled GEMM (dense, grouped) as exact per-group float64 sums.
   accsim   limited-precision accumulator model for the K = 4096 demonstration.
   norm     RMS / layer normalization whose binary32 output feeds the 1x128 cast.
+  moe      FP8 dispatch: quantize tokens, permute into the padded per-expert layout.
 """
 
 from . import e4m3, bf16, quant, gemm, accsim  # noqa: F401
