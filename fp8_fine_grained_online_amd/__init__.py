@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   fp8_gemm_blockscaled(a, sa, b, sb, out_dtype)          -> c
   fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype)   -> c
   fp8q_norm_quant_act_1x128(x, gamma, eps, beta, centred) -> (q, sa)   normalization + cast
+  fp8q_moe_dispatch_1x128(x, topk_ids, G) -> (q, sa, m_offsets, row_of_slot)   MoE FP8 dispatch
 Backward pass (Dgrad dX = dY W, Wgrad dW = dY^T X):
   fp8q_quant_act_128x1(x)                    -> (qt, st)   128x1 tiles, transposed
   fp8q_quant_act_1x128_128x1(x)              -> (q, sa, qt, st)   both, one read of x
@@ -32,6 +33,7 @@ from ._lib import (  # noqa: F401
     fp8q_quant_act_128x1,
     fp8q_quant_act_1x128_128x1,
     fp8q_norm_quant_act_1x128,
+    fp8q_moe_dispatch_1x128,
     fp8q_quant_act_1x128,
     fp8q_requant_1x128_to_128x1,
     fp8q_transpose_weight_128x128,
@@ -45,6 +47,6 @@ __all__ = [
     "Fp8qError", "FP8Q_OUT_BF16", "FP8Q_OUT_F32", "STATUS",
     "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
     "fp8_gemm_blockscaled", "fp8_gemm_grouped", "fp8q_version", "lib", "lib_path",
-    "fp8q_quant_act_128x1", "fp8q_quant_act_1x128_128x1", "fp8q_norm_quant_act_1x128", "fp8q_requant_1x128_to_128x1", "fp8q_transpose_weight_128x128",
+    "fp8q_quant_act_128x1", "fp8q_quant_act_1x128_128x1", "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8q_requant_1x128_to_128x1", "fp8q_transpose_weight_128x128",
     "fp8_gemm_rowscaled",
 ]

@@ -51,6 +51,13 @@ def lib() -> ctypes.CDLL:
         L.fp8_gemm_grouped.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, vp]
         L.fp8q_quant_act_128x1.restype = i32
         L.fp8q_quant_act_128x1.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fp8q_moe_dispatch_1x128.restype = i32
+        L.fp8q_moe_dispatch_1x128.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, i64, vp, vp, vp,
+                                              i64, vp]
+        L.fp8q_moe_dispatch_workspace_bytes.restype = i64
+        L.fp8q_moe_dispatch_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fp8q_moe_dispatch_max_rows.restype = i64
+        L.fp8q_moe_dispatch_max_rows.argtypes = [i64, i64, i64]
         L.fp8q_norm_quant_act_1x128.restype = i32
         L.fp8q_norm_quant_act_1x128.argtypes = [vp, vp, vp, ctypes.c_float, i32, i64, i64, vp, vp, vp]
         L.fp8q_quant_act_1x128_128x1.restype = i32
@@ -196,6 +203,8 @@ def fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype="bf16", c=None, M_total=
     M = a.shape[0] if M_total is None else int(M_total)
     if a.shape[1] != K or a.shape[0] < M:
         raise ValueError("a must be at least M_total x K")
+    if K % 128 == 0 and (sa.shape[0] < M or sa.shape[1] != K // 128):
+        raise ValueError("sa must be at least M_total x K/128")
     c = _out(c, "c", (M, N), tdt, a.device)
     _check("fp8_gemm_grouped",
            lib().fp8_gemm_grouped(pa, psa, pb, psb, c.data_ptr(), code, poff, G, M, N, K,
@@ -217,6 +226,39 @@ def fp8q_quant_act_128x1(x, qt=None, st=None, stream=None):
     _check("fp8q_quant_act_128x1",
            lib().fp8q_quant_act_128x1(px, M, K, qt.data_ptr(), st.data_ptr(), _stream(stream)))
     return qt, st
+
+
+def fp8q_moe_dispatch_1x128(x, topk_ids, G, q=None, sa=None, m_offsets=None, row_of_slot=None,
+                            workspace=None, stream=None):
+    """FP8 dispatch: x bf16 T x K, topk_ids int32 T x topk (device) ->
+    (q uint8 M_cap x K, sa float32 M_cap x K/128, m_offsets int32[G+1], row_of_slot int32 T x topk).
+
+    M_cap = fp8q_moe_dispatch_max_rows(T, topk, G); only rows below m_offsets[G]
+    are written. Pass q.shape[0] as M_total to fp8_gemm_grouped (no host sync).
+    """
+    torch = _torch()
+    px = _dev(x, "x", torch.bfloat16, 2)
+    pid = _dev(topk_ids, "topk_ids", torch.int32, 2)
+    T, K = x.shape
+    if topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must have one row per token")
+    topk = topk_ids.shape[1]
+    L = lib()
+    M_cap = L.fp8q_moe_dispatch_max_rows(T, topk, G)
+    ws_bytes = L.fp8q_moe_dispatch_workspace_bytes(T, topk, G)
+    if M_cap < 0 or ws_bytes < 0:
+        raise ValueError("invalid dispatch sizes")
+    q = _out(q, "q", (M_cap, K), torch.uint8, x.device)
+    sa = _out(sa, "sa", (M_cap, _div128(K)), torch.float32, x.device)
+    m_offsets = _out(m_offsets, "m_offsets", (G + 1,), torch.int32, x.device)
+    row_of_slot = _out(row_of_slot, "row_of_slot", (T, topk), torch.int32, x.device)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=x.device)
+    _check("fp8q_moe_dispatch_1x128",
+           L.fp8q_moe_dispatch_1x128(px, pid, T, K, topk, G, q.data_ptr(), sa.data_ptr(), M_cap,
+                                     m_offsets.data_ptr(), row_of_slot.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return q, sa, m_offsets, row_of_slot
 
 
 def fp8q_norm_quant_act_1x128(x, gamma, eps, beta=None, centred=False, q=None, sa=None,

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfp8q.so")
 
-SOURCES = ["quant.hip", "retile.hip", "norm.hip", "gemm.hip", "api.cpp"]
+SOURCES = ["quant.hip", "retile.hip", "norm.hip", "moe.hip", "gemm.hip", "api.cpp"]
 HEADERS = ["common.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -29,6 +29,10 @@ hipError_t launch_quant_act_128x1(const void* x, int64_t M, int64_t K, uint8_t* 
 hipError_t launch_norm_quant_act_1x128(const void* x, const void* gamma, const void* beta,
                                        float eps, bool centred, int64_t M, int64_t K, uint8_t* q,
                                        float* sa, hipStream_t stream);
+int64_t dispatch_workspace_bytes(int64_t slots, int64_t G);
+hipError_t launch_moe_dispatch(const void* x, const int32_t* ids, int64_t T, int64_t K, int64_t k,
+                               int64_t G, uint8_t* q, float* sa, int32_t* m_offsets,
+                               int32_t* row_of_slot, void* workspace, hipStream_t stream);
 hipError_t launch_quant_act_dual(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
                                  uint8_t* qt, float* st, hipStream_t stream);
 hipError_t launch_requant_1x128_to_128x1(const uint8_t* q, const float* sa, int64_t M, int64_t K,
@@ -44,6 +48,7 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;  // kernels index rows/cols 
 // GEMM operand tiles (up to 256 rows of K bytes) are addressed with 32-bit
 // offsets through buffer descriptors
 constexpr int64_t kMaxK = int64_t(1) << 23;
+constexpr int64_t kMaxExperts = 1024;  // dispatch: one scan thread per expert
 // the fused normalization keeps a row in one wavefront's registers
 constexpr int64_t kNormMaxK = 16384;
 constexpr int kMaxDevices = 64;
@@ -83,6 +88,13 @@ int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const
   if (K > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(sa, 4) || !aligned(sb, 4)))
     return FP8Q_ERR_ALIGN;
   return FP8Q_OK;
+}
+
+// worst-case m_offsets[G] of the MoE dispatch (every expert padded by 127
+// rows), rounded up to a multiple of 128 so that it is a valid M_total for
+// the grouped GEMM
+int64_t dispatch_max_rows(int64_t T, int64_t topk, int64_t G) {
+  return (T * topk + (kGroup - 1) * G + kGroup - 1) / kGroup * kGroup;
 }
 
 // Checks shared by the three 128 x 128 tile re-tiling calls (R x C -> C x R).
@@ -171,6 +183,40 @@ int fp8q_quant_act_128x1(const void* x_bf16, int64_t M, int64_t K, uint8_t* qt, 
   if (s == -1) return FP8Q_OK;
   if (s || (s = check_device())) return s;
   return launched(fp8q::launch_quant_act_128x1(x_bf16, M, K, qt, st, (hipStream_t)stream));
+}
+
+int64_t fp8q_moe_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t G) {
+  if (T < 0 || topk < 1 || G < 1 || G > kMaxExperts) return -1;
+  if (T > kMaxDim / topk) return -1;
+  return fp8q::dispatch_workspace_bytes(T * topk, G);
+}
+
+int64_t fp8q_moe_dispatch_max_rows(int64_t T, int64_t topk, int64_t G) {
+  if (T < 0 || topk < 1 || G < 1 || G > kMaxExperts) return -1;
+  if (T > kMaxDim / topk) return -1;
+  return dispatch_max_rows(T, topk, G);
+}
+
+int fp8q_moe_dispatch_1x128(const void* x_bf16, const int32_t* topk_ids, int64_t T, int64_t K,
+                            int64_t topk, int64_t G, uint8_t* q, float* sa, int64_t M_cap,
+                            int32_t* m_offsets, int32_t* row_of_slot, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  if (T < 0 || K < 0 || K % kGroup || topk < 1 || G < 1) return FP8Q_ERR_SHAPE;
+  if (G > kMaxExperts || K > kMaxDim || T > kMaxDim / topk) return FP8Q_ERR_TOO_LARGE;
+  const int64_t need_rows = dispatch_max_rows(T, topk, G);
+  if (need_rows > kMaxDim || T > kMaxDim / 4) return FP8Q_ERR_TOO_LARGE;
+  if (M_cap < need_rows) return FP8Q_ERR_SHAPE;  // outputs too small for the worst-case padding
+  if (!m_offsets || !workspace) return FP8Q_ERR_NULL;
+  if (T > 0 && (!topk_ids || !row_of_slot)) return FP8Q_ERR_NULL;
+  if (K > 0 && (!q || !sa || (T > 0 && !x_bf16))) return FP8Q_ERR_NULL;
+  if (workspace_bytes < fp8q::dispatch_workspace_bytes(T * topk, G)) return FP8Q_ERR_SHAPE;
+  if (!aligned(m_offsets, 4) || !aligned(workspace, 4)) return FP8Q_ERR_ALIGN;
+  if (T > 0 && (!aligned(topk_ids, 4) || !aligned(row_of_slot, 4))) return FP8Q_ERR_ALIGN;
+  if (K > 0 && (!aligned(q, 16) || !aligned(sa, 4) || (T > 0 && !aligned(x_bf16, 16))))
+    return FP8Q_ERR_ALIGN;
+  if (int s = check_device()) return s;
+  return launched(fp8q::launch_moe_dispatch(x_bf16, topk_ids, T, K, topk, G, q, sa, m_offsets,
+                                            row_of_slot, workspace, (hipStream_t)stream));
 }
 
 int fp8q_norm_quant_act_1x128(const void* x_bf16, const void* gamma_bf16, const void* beta_bf16,

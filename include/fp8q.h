@@ -142,8 +142,12 @@ FP8Q_API int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8
  *   sb        : in,  G x (N/128) x (K/128) float32
  *   c         : out, M_total x N (float32 or bfloat16)
  *   m_offsets : in,  DEVICE int32[G+1]; m_offsets[0] = 0, nondecreasing,
- *               every entry a multiple of 128, m_offsets[G] = M_total
- *   M_total   : host copy of m_offsets[G] (sizes the launch; no device read)
+ *               every entry a multiple of 128, m_offsets[G] <= M_total
+ *   M_total   : host-side row count of a and c, at least m_offsets[G] (sizes
+ *               the launch; no device read). Rows from m_offsets[G] to
+ *               M_total are neither read nor written, so the output of
+ *               fp8q_moe_dispatch_1x128 can be passed with its capacity as
+ *               M_total and no host synchronization.
  * Offsets that break these rules are outside the contract: rows are then
  * assigned to experts by the (clamped) offsets, and no access leaves the
  * buffers sized by M_total, G, N and K.
@@ -151,6 +155,52 @@ FP8Q_API int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8
 FP8Q_API int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                      void* c, int out_dtype, const int32_t* m_offsets, int64_t G,
                      int64_t M_total, int64_t N, int64_t K, void* stream);
+
+/*
+ * FP8 dispatch of MoE tokens on one GPU: quantize every token once (1x128
+ * tiles, the rule of fp8q_quant_act_1x128) and place its codes and scales in
+ * the row block of each expert the router chose, in the padded per-expert
+ * layout fp8_gemm_grouped consumes.
+ * Source: "Six Reasons Deepseek Ai Is A Waste Of Time", the paragraph on the
+ * combine and dispatch components (activations quantized to FP8 before the
+ * MoE up-projections, then dispatched); the grouped layout of item 8 of the
+ * Japanese codingmall.com page. The all-to-all between GPUs is not part of
+ * this call.
+ *
+ * A slot (t, j) = topk_ids[t * topk + j] is valid when 0 <= id < G; invalid
+ * choices are dropped. counts[e] = valid slots choosing e;
+ * m_offsets[0] = 0, m_offsets[e+1] = m_offsets[e] + roundup(counts[e], 128).
+ * Expert e's valid slots, in increasing slot order, take rows m_offsets[e],
+ * m_offsets[e] + 1, ...; row_of_slot[t * topk + j] is that row, or -1.
+ * Row r of (q, sa) holds the 1x128 codes and scales of its token; the padding
+ * rows m_offsets[e] + counts[e] .. m_offsets[e+1]-1 are zero (codes and
+ * scales). Rows from m_offsets[G] to M_cap are not written.
+ *
+ *   x_bf16      : in,  T x K bfloat16, 16-byte aligned
+ *   topk_ids    : in,  DEVICE int32 T x topk, 4-byte aligned
+ *   q, sa       : out, M_cap x K E4M3 (16-byte aligned), M_cap x (K/128) float32
+ *   M_cap       : rows of q and sa; at least fp8q_moe_dispatch_max_rows(T, topk, G)
+ *                 = T * topk + 127 * G (the largest possible m_offsets[G])
+ *                 rounded up to a multiple of 128
+ *   m_offsets   : out, DEVICE int32[G+1]
+ *   row_of_slot : out, DEVICE int32 T x topk (the map a combine step inverts)
+ *   workspace   : DEVICE scratch of at least
+ *                 fp8q_moe_dispatch_workspace_bytes(T, topk, G) bytes, 4-byte
+ *                 aligned, owned by the caller; no contents needed on entry
+ * Requires K % 128 == 0, topk >= 1, 1 <= G <= 1024. T == 0 still writes
+ * m_offsets (all zero). Five kernels are enqueued on `stream`.
+ */
+FP8Q_API int fp8q_moe_dispatch_1x128(const void* x_bf16, const int32_t* topk_ids, int64_t T,
+                                     int64_t K, int64_t topk, int64_t G, uint8_t* q, float* sa,
+                                     int64_t M_cap, int32_t* m_offsets, int32_t* row_of_slot,
+                                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace fp8q_moe_dispatch_1x128 needs (-1 for invalid sizes). */
+FP8Q_API int64_t fp8q_moe_dispatch_workspace_bytes(int64_t T, int64_t topk, int64_t G);
+
+/* Rows the dispatch outputs must hold: T * topk + 127 * G rounded up to a
+ * multiple of 128, a valid M_total for fp8_gemm_grouped (-1 for invalid sizes). */
+FP8Q_API int64_t fp8q_moe_dispatch_max_rows(int64_t T, int64_t topk, int64_t G);
 
 /*
  * Layer normalization fused with the 1x128 activation quantization.

@@ -68,5 +68,6 @@ def dispatch_1x128(x_bits, topk_ids, G: int):
 
 
 def max_rows(T: int, k: int, G: int) -> int:
-    """Upper bound on m_offsets[G]: every expert adds at most 127 padding rows."""
-    return T * k + (GROUP - 1) * G
+    """Upper bound on m_offsets[G] (every expert adds at most 127 padding rows),
+    rounded up to a multiple of 128."""
+    return (T * k + (GROUP - 1) * G + GROUP - 1) // GROUP * GROUP

@@ -27,7 +27,7 @@ def declared_symbols():
 ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
                 "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
                 "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1",
-                "fp8q_norm_quant_act_1x128"]
+                "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128"]
 
 
 def test_header_declares_the_entry_points():
@@ -187,6 +187,42 @@ def test_norm_quant_validation():
     assert f(None, None, None, 1e-6, 0, 0, 128, None, None, None) == 0
 
 
+def test_dispatch_sizes_and_validation():
+    import ctypes
+    L = _lib()
+    assert L.fp8q_moe_dispatch_max_rows(8192, 8, 32) == (8192 * 8 + 127 * 32 + 127) // 128 * 128
+    assert L.fp8q_moe_dispatch_max_rows(1, 1, 1) == 128
+    assert L.fp8q_moe_dispatch_max_rows(10, 0, 32) == -1
+    assert L.fp8q_moe_dispatch_max_rows(10, 2, 1025) == -1
+    ws = L.fp8q_moe_dispatch_workspace_bytes(8192, 8, 32)
+    assert ws == (2 * (8192 * 8 // 256) * 32 + 32) * 4
+    assert L.fp8q_moe_dispatch_workspace_bytes(-1, 8, 32) == -1
+    f = L.fp8q_moe_dispatch_1x128
+    OFFS, ROWS, WS = OFF, A, C
+    cap = L.fp8q_moe_dispatch_max_rows(64, 2, 4)
+    wsb = L.fp8q_moe_dispatch_workspace_bytes(64, 2, 4)
+    ok = [X, SB, 64, 256, 2, 4, Q, SA, cap, OFFS, ROWS, WS, wsb, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["x", "ids", "T", "K", "topk", "G", "q", "sa", "cap", "off", "rows", "ws", "wsb", "s"]
+        for k_, v in kw.items():
+            args[names.index(k_)] = v
+        return f(*args)
+
+    assert call(K=100) == 2 and call(topk=0) == 2 and call(G=0) == 2 and call(T=-1) == 2
+    assert call(G=1025) == 7
+    assert call(cap=cap - 1) == 2                      # outputs too small for the padding
+    assert call(wsb=wsb - 4) == 2                      # workspace too small
+    for name in ["x", "ids", "q", "sa", "off", "rows", "ws"]:
+        assert call(**{name: None}) == 1, name
+    assert call(x=X + 8) == 3 and call(q=Q + 4) == 3 and call(ids=SB + 2) == 3
+    assert call(sa=SA + 2) == 3 and call(off=OFFS + 2) == 3 and call(ws=WS + 2) == 3
+    # T = 0 needs no token pointers but still writes m_offsets
+    assert call(T=0, x=None, ids=None, rows=None, cap=L.fp8q_moe_dispatch_max_rows(0, 2, 4),
+                wsb=L.fp8q_moe_dispatch_workspace_bytes(0, 2, 4)) in (0, 6)
+
+
 def test_rowscaled_gemm_validation():
     L = _lib()
     f = L.fp8_gemm_rowscaled
@@ -210,6 +246,8 @@ def test_valid_call_without_gpu_reports_no_device():
     assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
     assert L.fp8q_quant_act_1x128_128x1(X, 128, 128, Q, SA, B, SB, None) == 6
     assert L.fp8q_norm_quant_act_1x128(X, B, None, 1e-6, 0, 4, 128, Q, SA, None) == 6
+    assert L.fp8q_moe_dispatch_1x128(X, SB, 64, 256, 2, 4, Q, SA, 640, OFF, A, C,
+                                     L.fp8q_moe_dispatch_workspace_bytes(64, 2, 4), None) == 6
     assert L.fp8q_requant_1x128_to_128x1(X, SA, 128, 128, Q, SB, None) == 6
     assert L.fp8q_transpose_weight_128x128(X, SA, 128, 128, Q, SB, None) == 6
     assert L.fp8_gemm_rowscaled(A, SA, B, SB, C, 0, 64, 128, 128, None) == 6
