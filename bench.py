@@ -35,7 +35,8 @@ FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 # sources whose hash keys the recorded counters of each streaming kernel
 STREAM_SOURCES = {"quant_act_1x128": ("quant.hip", "common.hpp"),
-                  "norm_quant_act_1x128": ("norm.hip", "common.hpp")}
+                  "norm_quant_act_1x128": ("norm.hip", "common.hpp"),
+                  "moe_dispatch_1x128": ("moe.hip", "common.hpp")}
 
 
 def source_hash(*names):
@@ -267,6 +268,71 @@ def plan_stream(w, args, F, S, L, dev, sp, up_bf16):
     }
 
 
+def plan_dispatch(w, args, F, S, L, dev, sp, up_bf16):
+    """MoE FP8 dispatch (quantize + permute), optionally followed by the
+    expert weights' quantization and the grouped up-projection GEMM fed the
+    dispatch output with no host synchronization."""
+    import torch
+    T, K, G, k = w.M, w.K, w.G, w.topk
+    x_bits, ids, b_bits = S.dispatch_inputs(w, args.seed)
+    X = up_bf16(x_bits)
+    ids_d = torch.from_numpy(ids).to(dev)
+    cap = L.fp8q_moe_dispatch_max_rows(T, k, G)
+    ws_bytes = L.fp8q_moe_dispatch_workspace_bytes(T, k, G)
+    q = torch.empty((cap, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((cap, K // 128), dtype=torch.float32, device=dev)
+    off = torch.empty((G + 1,), dtype=torch.int32, device=dev)
+    rows = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    launches = [("moe_dispatch_1x128",
+                 lambda: L.fp8q_moe_dispatch_1x128(X.data_ptr(), ids_d.data_ptr(), T, K, k, G,
+                                                   q.data_ptr(), sa.data_ptr(), cap, off.data_ptr(),
+                                                   rows.data_ptr(), ws.data_ptr(), ws_bytes, sp))]
+    # real rows only: read x once, write every chosen row's codes and scales, the row map
+    nbytes = T * K * 2 + T * k * (K + (K // 128) * 4) + T * k * 4 * 2
+    config = {"workload": args.workload, "tokens": T, "K": K, "G": G, "topk": k,
+              "step": "moe_dispatch_1x128"}
+    if not w.N:
+        return {"launches": launches, "flops": {}, "bytes": {"moe_dispatch_1x128": nbytes},
+                "stream": "moe_dispatch_1x128", "config": config, "extra": {},
+                "cpu": lambda: cpu_baseline_dispatch(args.workload, x_bits, ids, G, 256)}
+    N = w.N
+    B = up_bf16(b_bits)
+    qb = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((G * N // 128, K // 128), dtype=torch.float32, device=dev)
+    C = torch.empty((cap, N), dtype=torch.bfloat16, device=dev)
+    launches += [
+        ("quant_weight_128x128",
+         lambda: L.fp8q_quant_weight_128x128(B.data_ptr(), G * N, K, qb.data_ptr(), sb.data_ptr(), sp)),
+        ("fp8_gemm_grouped",
+         lambda: L.fp8_gemm_grouped(q.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(),
+                                    C.data_ptr(), F.FP8Q_OUT_BF16, off.data_ptr(), G, cap, N, K, sp)),
+    ]
+    flops = 2.0 * T * k * N * K
+    config.update({"N": N, "out": "bf16",
+                   "step": "moe_dispatch_1x128 + quant_weight_128x128 + fp8_gemm_grouped "
+                           "(M_total = dispatch capacity, no host sync)"})
+    return {"launches": launches, "flops": {"fp8_gemm_grouped": flops}, "flops_step": flops,
+            "bytes": {"moe_dispatch_1x128": nbytes,
+                      "quant_weight_128x128": G * N * K * 3 + (G * N // 128) * (K // 128) * 4},
+            "config": config, "extra": {},
+            "cpu": lambda: cpu_baseline(args.workload + " expert 0", x_bits[:128], b_bits[0], 128)}
+
+
+def cpu_baseline_dispatch(workload, x_bits, ids, G, tokens):
+    """The oracle, untuned, dispatching the first `tokens` tokens."""
+    from oracle import moe
+    threads = oracle_threads()
+    t0 = time.perf_counter()
+    moe.dispatch_1x128(x_bits[:tokens], ids[:tokens], G)
+    dt = time.perf_counter() - t0
+    T, K = x_bits.shape
+    k = ids.shape[1]
+    nbytes = tokens * K * 2 + tokens * k * (K + (K // 128) * 4) + tokens * k * 8
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{workload}: oracle dispatch of the first {tokens} tokens; {dt:.2f} s"}
+
+
 def cpu_baseline_stream(workload, x_bits, bytes_per_row, rows, gamma_bits):
     """The oracle, untuned, on the first `rows` rows."""
     from oracle import norm, quant
@@ -358,7 +424,12 @@ def main():
     def up_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    kind = plan_backward if w.backward else (plan_stream if w.N == 0 else plan_forward)
+    if w.topk:
+        kind = plan_dispatch
+    elif w.backward:
+        kind = plan_backward
+    else:
+        kind = plan_stream if w.N == 0 else plan_forward
     plan = kind(w, args, F, S, L, dev, sp, up_bf16)
     launches = plan["launches"]
     names = [n for n, _ in launches]

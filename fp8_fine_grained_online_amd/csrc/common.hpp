@@ -39,6 +39,15 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   return v;
 }
 
+// max over the 8 lanes of each half DPP row (lanes 8r .. 8r+7)
+__device__ __forceinline__ uint32_t row8_max_u32(uint32_t v) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  return v;
+}
+
 // Per-tile quotient x / s, correctly rounded in binary32.
 //
 // The divide is replaced by a reciprocal and one FMA correction
@@ -93,6 +102,14 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
+}
+
+// max |x| over the 8 bf16 values of a 16-byte chunk
+__device__ __forceinline__ float absmax8(uint4 v) {
+  return fmaxf(fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                     fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))),
+               fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
+                     fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
 }
 
 // Quantize the 8 bf16 values in `in` (4 dwords) to 8 codes (2 dwords).

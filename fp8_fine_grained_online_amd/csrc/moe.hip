@@ -12,14 +12,15 @@
 // Row order inside an expert's block is slot order, slot = token * k + choice,
 // so the layout is deterministic. Five launches:
 //   count  per 256-slot block, a histogram of the valid choices (LDS atomics);
-//   scan   one workgroup: per-expert totals, padded offsets, and for every
-//          (block, expert) the first row that block's slots of that expert take;
+//   scan   one workgroup, 1024/G threads per expert: per-expert totals, padded
+//          offsets, and for every (block, expert) the first row that block's
+//          slots of that expert take;
 //   rank   per block: each wavefront ranks its 64 slots among equal experts
 //          (one ballot per distinct expert present), the 4 wavefronts' counts
 //          are added in LDS, and row = base + earlier waves + rank;
 //   quant  one wavefront per token: read and quantize the token once, store
 //          its codes and scales to each of its rows;
-//   pad    one workgroup per expert: zero its padding rows.
+//   pad    one workgroup per possible padding row (127 per expert): zero it.
 #include "common.hpp"
 
 namespace fp8q {
@@ -43,33 +44,59 @@ __global__ __launch_bounds__(kDispBlock) void dispatch_count_kernel(const int32_
   for (int e = threadIdx.x; e < G; e += kDispBlock) hist[(int64_t)blockIdx.x * G + e] = h[e];
 }
 
+// One workgroup. Thread (e, p) = (tid / tpe, tid % tpe), tpe = 1024 / G
+// threads per expert, owns the contiguous run of blocks [p * chunk, (p+1) *
+// chunk) of expert e's column of the histogram: it sums them, the partial sums
+// of an expert are combined in LDS (totals, then a prefix over p), and the
+// thread writes the base row of each of its blocks.
 __global__ __launch_bounds__(kMaxExperts) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int n_blk, int G, int32_t* __restrict__ base,
     int32_t* __restrict__ counts, int32_t* __restrict__ m_offsets) {
-  __shared__ int32_t padded[kMaxExperts];
+  __shared__ int32_t part[kMaxExperts];  // [e * tpe + p]
   __shared__ int32_t off[kMaxExperts + 1];
-  const int e = threadIdx.x;
-  if (e < G) {
+  const int tpe = kMaxExperts / G;
+  const int e = threadIdx.x / tpe, p = threadIdx.x % tpe;
+  const bool on = e < G;
+  const int chunk = (n_blk + tpe - 1) / tpe;
+  const int b0 = min(p * chunk, n_blk), b1 = min(b0 + chunk, n_blk);
+  int sum = 0;
+  if (on) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) sum += hist[(int64_t)b * G + e];
+    part[e * tpe + p] = sum;
+  }
+  __syncthreads();
+  // expert totals (thread p = 0 of each expert), then an inclusive scan of the
+  // padded totals over all 1024 threads (Hillis-Steele in LDS)
+  __shared__ int32_t scan[kMaxExperts];
+  int padded = 0;
+  if (on && p == 0) {
     int total = 0;
-    for (int b = 0; b < n_blk; ++b) total += hist[(int64_t)b * G + e];
+    for (int q = 0; q < tpe; ++q) total += part[e * tpe + q];
     counts[e] = total;
-    padded[e] = (total + kGroup - 1) / kGroup * kGroup;
+    padded = (total + kGroup - 1) / kGroup * kGroup;
   }
+  const int tid = threadIdx.x;
+  const int slot_e = (on && p == 0) ? e : -1;  // each expert's total sits at index e
+  scan[tid] = 0;
   __syncthreads();
-  if (e == 0) {
-    int run = 0;
-    for (int i = 0; i < G; ++i) {
-      off[i] = run;
-      run += padded[i];
-    }
-    off[G] = run;
+  if (slot_e >= 0) scan[slot_e] = padded;
+  __syncthreads();
+  for (int d = 1; d < kMaxExperts; d <<= 1) {
+    const int v = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
   }
+  if (tid < G) off[tid + 1] = scan[tid];
+  if (tid == 0) off[0] = 0;
   __syncthreads();
-  if (e < G) m_offsets[e] = off[e];
-  if (e == 0) m_offsets[G] = off[G];
-  if (e < G) {
+  if (threadIdx.x < G) m_offsets[threadIdx.x] = off[threadIdx.x];
+  if (threadIdx.x == 0) m_offsets[G] = off[G];
+  if (on) {
     int run = off[e];
-    for (int b = 0; b < n_blk; ++b) {
+    for (int q = 0; q < p; ++q) run += part[e * tpe + q];
+    for (int b = b0; b < b1; ++b) {
       const int64_t i = (int64_t)b * G + e;
       const int c = hist[i];
       base[i] = run;
@@ -113,8 +140,10 @@ __global__ __launch_bounds__(kDispBlock) void dispatch_rank_kernel(const int32_t
   }
 }
 
-// One wavefront per token; a 1x128 tile is 16 chunks of 16 bytes = one DPP
-// row of 16 lanes, so 64 lanes quantize 4 tiles per step.
+// One wavefront per token. Lane l owns 16 consecutive values (32 bytes in, 16
+// bytes of codes out) of each 1024-value step, so a 1x128 tile is 8 lanes
+// (half a DPP row) and every destination row gets one 16-byte store per lane
+// and one 32-byte run of 8 scales per step.
 __global__ __launch_bounds__(256) void dispatch_quant_kernel(const uint4* __restrict__ x, int T,
                                                              int K, int k,
                                                              const int32_t* __restrict__ row_of_slot,
@@ -127,42 +156,50 @@ __global__ __launch_bounds__(256) void dispatch_quant_kernel(const uint4* __rest
   const int G = K / kGroup;
   const uint4* xr = x + (int64_t)t * n_chunks;
   const int32_t* rows = row_of_slot + (int64_t)t * k;
-  for (int c0 = 0; c0 < n_chunks; c0 += 64) {
-    const int c = c0 + lane;
-    const bool have = c < n_chunks;  // whole tiles (DPP rows) are present or absent
-    const uint4 v = have ? load_nt(xr + c) : make_uint4(0, 0, 0, 0);
-    float m = 0.0f;
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
-                       fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
-                       fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
-    const float amax = __uint_as_float(row16_max_u32(__float_as_uint(m)));
-    const float s = __fdiv_rn(amax, kFp8Max);
-    const TileDivisor d = make_divisor(s, amax);
-    const uint2 codes = quant8(v, d);
-    if (have) {
-      for (int j = 0; j < k; ++j) {
-        const int row = rows[j];  // same for the whole wavefront
-        if (row < 0) continue;   // dropped choice
-        q[(int64_t)row * n_chunks + c] = codes;
-        if ((lane & 15) == 0) sa[(int64_t)row * G + (c >> 4)] = s;
+  constexpr int kBatch = 2;  // steps whose loads are in flight together
+  for (int p0 = 0; p0 < n_chunks; p0 += 128 * kBatch) {
+    uint4 v[kBatch][2];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = p0 + 128 * u + 2 * lane;  // this lane's first chunk
+      const bool have = c < n_chunks;         // whole tiles (8 lanes) are present or absent
+      v[u][0] = have ? load_nt(xr + c) : make_uint4(0, 0, 0, 0);
+      v[u][1] = have ? load_nt(xr + c + 1) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = p0 + 128 * u + 2 * lane;
+      const bool have = c < n_chunks;
+      const float m = fmaxf(absmax8(v[u][0]), absmax8(v[u][1]));
+      const float amax = __uint_as_float(row8_max_u32(__float_as_uint(m)));
+      const float s = __fdiv_rn(amax, kFp8Max);
+      const TileDivisor d = make_divisor(s, amax);
+      const uint2 lo = quant8(v[u][0], d), hi = quant8(v[u][1], d);
+      const uint4 codes = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      if (have) {
+        for (int j = 0; j < k; ++j) {
+          const int row = rows[j];  // same for the whole wavefront
+          if (row < 0) continue;   // dropped choice
+          *(uint4*)(q + ((int64_t)row * n_chunks + c)) = codes;
+          if ((lane & 7) == 0) sa[(int64_t)row * G + (c >> 4)] = s;
+        }
       }
     }
   }
 }
 
+// grid (127, G): workgroup (i, e) zeroes padding row i of expert e, if it exists
 __global__ __launch_bounds__(256) void dispatch_pad_kernel(const int32_t* __restrict__ m_offsets,
                                                            const int32_t* __restrict__ counts,
                                                            int K, uint4* __restrict__ q,
                                                            float* __restrict__ sa) {
-  const int e = blockIdx.x;
-  const int64_t r0 = (int64_t)m_offsets[e] + counts[e];
-  const int64_t n_rows = (int64_t)m_offsets[e + 1] - r0;  // at most 127
+  const int e = blockIdx.y;
+  const int64_t row = (int64_t)m_offsets[e] + counts[e] + blockIdx.x;
+  if (row >= m_offsets[e + 1]) return;  // at most 127 padding rows per expert
   const int n16 = K / 16;
-  for (int64_t i = threadIdx.x; i < n_rows * n16; i += 256)
-    q[(r0 + i / n16) * n16 + i % n16] = make_uint4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < n16; i += 256) q[row * n16 + i] = make_uint4(0, 0, 0, 0);
   const int G = K / kGroup;
-  for (int64_t i = threadIdx.x; i < n_rows * G; i += 256) sa[(r0 + i / G) * G + i % G] = 0.0f;
+  for (int i = threadIdx.x; i < G; i += 256) sa[row * G + i] = 0.0f;
 }
 
 int64_t dispatch_blocks(int64_t slots) { return (slots + kDispBlock - 1) / kDispBlock; }
@@ -191,8 +228,8 @@ hipError_t launch_moe_dispatch(const void* x, const int32_t* ids, int64_t T, int
     if (T > 0)
       hipLaunchKernelGGL(dispatch_quant_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
                          (const uint4*)x, (int)T, (int)K, (int)k, row_of_slot, (uint2*)q, sa);
-    hipLaunchKernelGGL(dispatch_pad_kernel, dim3((unsigned)G), dim3(256), 0, stream, m_offsets,
-                       counts, (int)K, (uint4*)q, sa);
+    hipLaunchKernelGGL(dispatch_pad_kernel, dim3(kGroup - 1, (unsigned)G), dim3(256), 0, stream,
+                       m_offsets, counts, (int)K, (uint4*)q, sa);
   }
   return hipGetLastError();
 }

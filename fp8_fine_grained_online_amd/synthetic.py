@@ -86,6 +86,7 @@ class Workload:
     G: int = 0  # experts (grouped); 0 = dense
     tokens: int = 0  # grouped: real tokens before padding
     backward: bool = False  # Dgrad + Wgrad of the layer Y[M x N] = X[M x K] W[N x K]^T
+    topk: int = 0  # MoE dispatch: router choices per token (M = tokens)
 
 
 WORKLOADS = {
@@ -98,6 +99,10 @@ WORKLOADS = {
     "skinny_64x7168x7168": Workload(30, "skinny_64x7168x7168", 64, 7168, 7168),
     "actquant_16384x7168": Workload(31, "actquant_16384x7168", 16384, 0, 7168),
     "normquant_16384x7168": Workload(32, "normquant_16384x7168", 16384, 0, 7168),
+    "dispatch_8192x7168_top8_g32": Workload(33, "dispatch_8192x7168_top8_g32", 8192, 0, 7168,
+                                            G=32, topk=8),
+    "moe_up_8192x4096x7168_top8_g32": Workload(34, "moe_up_8192x4096x7168_top8_g32", 8192, 4096,
+                                               7168, G=32, topk=8),
     "moe_g32_65536x4096x7168": Workload(4, "moe_g32_65536x4096x7168", 0, 4096, 7168,
                                         G=32, tokens=65536),
 }
@@ -119,6 +124,22 @@ def norm_params(K: int, rng: np.random.Generator):
     g = f32_to_bf16_bits(1.0 + 0.1 * rng.standard_normal(K, dtype=np.float32))
     b = f32_to_bf16_bits(0.05 * rng.standard_normal(K, dtype=np.float32))
     return g, b
+
+
+def routing(T: int, k: int, G: int, rng: np.random.Generator) -> np.ndarray:
+    """Router choices T x k (int32): k distinct experts per token, uniform."""
+    return np.argsort(rng.random((T, G)), axis=1)[:, :k].astype(np.int32)
+
+
+def dispatch_inputs(w: Workload, seed: int = 0):
+    """(x bits T x K, topk_ids T x k, expert weights G x N x K or None)."""
+    x = activations(w.M, w.K, rng_for(w.wid, T_A, seed))
+    ids = routing(w.M, w.topk, w.G, rng_for(w.wid, T_OFFSETS, seed))
+    b = None
+    if w.N:
+        rb = rng_for(w.wid, T_B, seed)
+        b = np.stack([weights(w.N, w.K, rb) for _ in range(w.G)])
+    return x, ids, b
 
 
 def backward_inputs(w: Workload, seed: int = 0):

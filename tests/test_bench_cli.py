@@ -48,6 +48,17 @@ def test_cpu_baseline_legs_on_tiny_inputs():
         assert d["unit"] == "GB/s" and d["kind"] == "oracle" and d["value"] > 0
 
 
+def test_dispatch_inputs_and_baseline():
+    import bench
+    from fp8_fine_grained_online_amd import synthetic as S
+    w = S.Workload(33, "small", 64, 0, 256, G=8, topk=3)
+    x, ids, b = S.dispatch_inputs(w)
+    assert x.shape == (64, 256) and ids.shape == (64, 3) and b is None
+    assert all(len(set(r)) == 3 for r in ids.tolist()) and ids.min() >= 0 and ids.max() < 8
+    d = bench.cpu_baseline_dispatch("small", x, ids, 8, 32)
+    assert d["unit"] == "GB/s" and d["kind"] == "oracle" and d["value"] > 0
+
+
 def test_backward_workload_inputs_have_the_layer_shapes():
     from fp8_fine_grained_online_amd import synthetic as S
     w = S.WORKLOADS["bwd_proj_8192x7168x2048"]
