@@ -56,7 +56,26 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
+    build_probes(verbose)
     return LIB_PATH
+
+
+# Test-only GPU probes (tests/probes/*.hip), each built into its own shared
+# library next to its source; the product library never loads them.
+PROBE_DIR = os.path.join(ROOT, "tests", "probes")
+
+
+def build_probes(verbose: bool = False):
+    if not os.path.isdir(PROBE_DIR):
+        return []
+    out = []
+    for src in sorted(f for f in os.listdir(PROBE_DIR) if f.endswith(".hip")):
+        lib = os.path.join(PROBE_DIR, "lib" + src[:-4] + ".so")
+        _run([HIPCC, *FLAGS, "-shared", "-x", "hip", os.path.join(PROBE_DIR, src), "-o", lib + ".tmp"],
+             verbose)
+        os.replace(lib + ".tmp", lib)
+        out.append(lib)
+    return out
 
 
 if __name__ == "__main__":
