@@ -158,8 +158,9 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
     def cpu():
         if grouped:
             r0 = int(off[0])
-            return cpu_baseline(args.workload + " expert 0", a_bits[r0:r0 + 128], b_bits[0], 128)
-        return cpu_baseline(args.workload, a_bits, b_bits, min(M, 1024))
+            n0 = int(off[1] - off[0])
+            return cpu_baseline(args.workload + " expert 0", a_bits[r0:r0 + n0], b_bits[0], n0)
+        return cpu_baseline(args.workload, a_bits, b_bits, min(M, 4096))
 
     return {
         "launches": launches,
