@@ -162,10 +162,14 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
             return cpu_baseline(args.workload + " expert 0", a_bits[r0:r0 + n0], b_bits[0], n0)
         return cpu_baseline(args.workload, a_bits, b_bits, min(M, 4096))
 
+    # algorithmic bytes of the GEMM: operands, scales and output, each once
+    gemm_bytes = (M * K + b_rows * K + M * (K // 128) * 4 + (b_rows // 128) * (K // 128) * 4
+                  + 2 * M * N)
     return {
         "launches": launches,
         "flops": {gemm_name: flops},
         "flops_step": flops,
+        "gemm_bytes": {gemm_name: gemm_bytes},
         "bytes": {"quant_act_1x128": M * K * 3 + M * (K // 128) * 4,
                   "quant_weight_128x128": b_rows * K * 3 + (b_rows // 128) * (K // 128) * 4},
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "G": w.G or None,
@@ -482,15 +486,25 @@ def main():
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(args.workload, STREAM_SOURCES[name])}
     else:
-        # the roofline kernel: the slowest contraction of the step
+        # the roofline kernel: the slowest contraction of the step; its roof is
+        # the MFMA peak unless its arithmetic intensity (FLOP per algorithmic
+        # byte) is below the ridge point, as for small-M shapes
         gemm_name = max(plan["flops"], key=lambda n: kms[n])
         gemm_tflops = plan["flops"][gemm_name] / (kms[gemm_name] * 1e-3) / 1e12
         metric = METRIC
         value, unit = plan["flops_step"] / (ms_step * 1e-3) / 1e12, "TFLOP/s"
-        roofline = {"bound": "mfma", "kernel": gemm_name, "achieved": round(gemm_tflops, 2),
-                    "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(args.workload, ("gemm.hip", "common.hpp"))}
+        traffic = measured_traffic(args.workload, ("gemm.hip", "common.hpp"))
+        gbytes = plan.get("gemm_bytes", {}).get(gemm_name)
+        ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if gbytes and plan["flops"][gemm_name] / gbytes < ridge:
+            gbps = gbytes / (kms[gemm_name] * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "kernel": gemm_name, "achieved": round(gbps, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+                        "traffic": traffic, "tflops": round(gemm_tflops, 2)}
+        else:
+            roofline = {"bound": "mfma", "kernel": gemm_name, "achieved": round(gemm_tflops, 2),
+                        "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
 
     out = {
         "metric": metric,
