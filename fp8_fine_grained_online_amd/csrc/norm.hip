@@ -14,11 +14,13 @@
 //             r = fl32(1 / sqrt(var + eps)),
 //             y = fl32(fl32(fl32(fl32(x - fl32(mu)) r) g) + b)
 // with every float64 step correctly rounded (division, square root) and the
-// sums formed as double-double (error-free TwoSum per term, then a butterfly
-// across the wavefront whose every combination is symmetric, so all lanes hold
-// the same bits): the statistics are the correctly rounded exact sums, not a
-// function of the summation order. Then y is quantized per 1x128 tile with the
-// activation rule (amax, s = fl32(amax/448), codes of fl32(y/s)).
+// statistics equal to the correctly rounded exact sums, not a function of the
+// summation order: a fast plain float64 pass whose result is certified (see
+// certified_inv_std and the exponent-span test of the mean), with an
+// error-free double-double pass (TwoSum per term, then a butterfly across the
+// wavefront whose every combination is symmetric, so all lanes hold the same
+// bits) where the certificate fails. Then y is quantized per 1x128 tile with
+// the activation rule (amax, s = fl32(amax/448), codes of fl32(y/s)).
 //
 // Every rounding above must happen as written: the library is compiled with
 // floating-point contraction off, so no product is fused into the addition
@@ -71,6 +73,49 @@ __device__ __forceinline__ float inv_std(double stat_over_k, float eps) {
   return (float)__ddiv_rn(1.0, __dsqrt_rn(t));
 }
 
+// Plain float64 sum over the wavefront; every combination is a symmetric
+// addition, so all lanes end with the same bits.
+__device__ __forceinline__ double wave_sum_plain(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = __dadd_rn(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m));
+  return v;
+}
+
+// The fast statistics are plain float64 sums of nonnegative terms with at
+// most 256 + 6 roundings in any chain (a lane's terms, then the butterfly),
+// so they are within a relative 263 * 2^-53 < 2^-44 of the exact sum, and the
+// exact sum's float64 rounding lies in S_fast * [1 - 2^-43, 1 + 2^-43]. Every
+// step from S to r (S/K, + eps, sqrt, 1/x, then to binary32) is correctly
+// rounded and monotone in S, so when both ends of that interval give the same
+// binary32 r, it is the r of the exact sum; otherwise the caller recomputes
+// the sum exactly (double-double). Returns true when r is certified.
+__device__ __forceinline__ bool certified_inv_std(double S_fast, int K, float eps, float& r) {
+  const double m = __dmul_rn(S_fast, 0x1p-43);
+  const float lo = inv_std(__ddiv_rn(__dadd_rn(S_fast, m), (double)K), eps);  // largest sum
+  const float hi = inv_std(__ddiv_rn(__dsub_rn(S_fast, m), (double)K), eps);  // smallest sum
+  r = lo;
+  return lo == hi;
+}
+
+// biased exponent field of a nonzero bf16 value, subnormals counted as 1 (they
+// are multiples of the same quantum as exponent 1); zeros give `none`
+__device__ __forceinline__ uint32_t bf16_exp_or(uint32_t half, uint32_t none) {
+  const uint32_t e = (half >> 7) & 0xFFu;
+  return (half & 0x7FFFu) ? (e ? e : 1u) : none;
+}
+
 // An empty asm that "modifies" the packed row: values unpacked from it before
 // cannot be reused after, so each pass re-unpacks (a few bit operations)
 // instead of keeping 8 floats or doubles per chunk live across passes.
@@ -113,19 +158,48 @@ __global__ __launch_bounds__(kNormThreads) void norm_quant_1x128_kernel(
   __syncthreads();
   if (!active) return;
 
+  // Statistics: a fast float64 pass whose result is certified exact, with an
+  // error-free double-double pass only where the certificate fails (rare:
+  // r within 2^-43 of a binary32 rounding boundary, or a centred row whose
+  // magnitudes span more than 31 binades).
   float r, mu32 = 0.0f;
   if constexpr (kCentred) {
-    DD s1{0.0, 0.0};
+    // The values of the row are multiples of 2^(emin - 134) below 2^(emax - 126);
+    // with K <= 2^14 every partial sum then fits in 53 bits when
+    // emax - emin <= 31, so the plain float64 sum is exact in any order.
+    double s1 = 0.0;
+    uint32_t emax = 0, emin = 255;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      float f[8];
-      unpack8(v[i], f);
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s1 = dd_add_term(s1, (double)f[e]);
+      for (int h = 0; h < 4; ++h) {
+        emax = max(emax, max(bf16_exp_or(w[h] & 0xFFFFu, 0u), bf16_exp_or(w[h] >> 16, 0u)));
+        emin = min(emin, min(bf16_exp_or(w[h] & 0xFFFFu, 255u), bf16_exp_or(w[h] >> 16, 255u)));
+        s1 = __dadd_rn(s1, (double)bf16_lo(w[h]));
+        s1 = __dadd_rn(s1, (double)bf16_hi(w[h]));
+      }
     }
-    const double mu = __ddiv_rn(wave_sum(s1), (double)K);
+    emax = wave_max_u32(emax);
+    emin = wave_min_u32(emin);
+    double S1;
+    if ((int)emax - (int)emin <= 31) {
+      S1 = wave_sum_plain(s1);
+    } else {
+      reunpack_fence(v);
+      DD d1{0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d1 = dd_add_term(d1, (double)f[e]);
+      }
+      S1 = wave_sum(d1);
+    }
+    const double mu = __ddiv_rn(S1, (double)K);
     reunpack_fence(v);
-    DD s2{0.0, 0.0};
+    double s2 = 0.0;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       if (lane + 64 * i >= n_chunks) continue;  // absent chunks would add mu^2
@@ -134,21 +208,47 @@ __global__ __launch_bounds__(kNormThreads) void norm_quant_1x128_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const double d = __dsub_rn((double)f[e], mu);
-        s2 = dd_add_term(s2, __dmul_rn(d, d));
+        s2 = __dadd_rn(s2, __dmul_rn(d, d));
       }
     }
-    r = inv_std(__ddiv_rn(wave_sum(s2), (double)K), eps);
+    if (!certified_inv_std(wave_sum_plain(s2), K, eps, r)) {
+      reunpack_fence(v);
+      DD d2{0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        if (lane + 64 * i >= n_chunks) continue;
+        float f[8];
+        unpack8(v[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double d = __dsub_rn((double)f[e], mu);
+          d2 = dd_add_term(d2, __dmul_rn(d, d));
+        }
+      }
+      r = inv_std(__ddiv_rn(wave_sum(d2), (double)K), eps);
+    }
     mu32 = (float)mu;
   } else {
-    DD s2{0.0, 0.0};
+    double s2 = 0.0;  // squares of bf16 values are exact in float64: one rounding per term
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       float f[8];
       unpack8(v[i], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s2 = dd_add_term(s2, __dmul_rn((double)f[e], (double)f[e]));
+      for (int e = 0; e < 8; ++e) s2 = __fma_rn((double)f[e], (double)f[e], s2);
     }
-    r = inv_std(__ddiv_rn(wave_sum(s2), (double)K), eps);
+    if (!certified_inv_std(wave_sum_plain(s2), K, eps, r)) {
+      reunpack_fence(v);
+      DD d2{0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d2 = dd_add_term(d2, __dmul_rn((double)f[e], (double)f[e]));
+      }
+      r = inv_std(__ddiv_rn(wave_sum(d2), (double)K), eps);
+    }
   }
 
   reunpack_fence(v);

@@ -88,3 +88,50 @@ def test_full_size_sampled_rows(centred):
     wq, ws = norm.norm_quant_act_1x128(x[rows], g, 1e-6, b, centred)
     assert np.array_equal(sa.cpu().numpy()[rows].view(np.uint32), ws.view(np.uint32))
     assert np.array_equal(q.cpu().numpy()[rows], wq)
+
+
+def eps_defeating_certificate(ms, seed=0, n=1 << 22):
+    """A binary32 eps for which r = 1/sqrt(ms + eps) (float64 steps) lies within
+    2^-45 r of a binary32 rounding midpoint, so that the kernel's fast,
+    certified statistics cannot decide r and its exact (double-double) path
+    must run. Found by a seeded search on the CPU."""
+    rng = np.random.default_rng(seed)
+    eps = rng.uniform(2.0 ** -20, 1.0, n).astype(np.float32)
+    r = 1.0 / np.sqrt(np.float64(ms) + eps.astype(np.float64))
+    r32 = r.astype(np.float32)
+    up = np.nextafter(r32, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(r32, np.float32(0)).astype(np.float64)
+    r32 = r32.astype(np.float64)
+    mid = np.where(r >= r32, (r32 + up) / 2, (r32 + dn) / 2)
+    d = np.abs(r - mid) / r
+    i = int(np.argmin(d))
+    assert d[i] < 2.0 ** -45
+    return float(eps[i])
+
+
+@pytest.mark.parametrize("a", [1.0, 3.0, 0.5])
+@pytest.mark.parametrize("centred", [False, True])
+def test_rows_whose_inverse_std_sits_on_a_rounding_boundary(a, centred):
+    """Rows with mean square a^2 (constant rows; for the centred form rows of
+    +-a, mean 0, variance a^2) and an eps that puts r within 2^-45 of a binary32
+    midpoint: the fast path's certificate fails and the exact path decides."""
+    K = 1024
+    eps = eps_defeating_certificate(a * a)
+    x = np.tile(bits(np.where(np.arange(K) % 2, a, -a) if centred else np.full(K, a)), (8, 1))
+    x[1::2] = S.activations(4, K, S.rng_for(986, int(a * 4)))  # ordinary rows beside them
+    g, b = params(K, 987)
+    check(x, g, b, eps, centred)
+
+
+def test_centred_rows_spanning_many_binades():
+    """Magnitudes spanning more than 31 binades: the plain float64 mean is not
+    exact, so the kernel sums the row in double-double."""
+    K = 2048
+    rng = S.rng_for(988, 0)
+    x = S.activations(6, K, rng)
+    x[0, 3] = bits([2.0 ** 40])[0]
+    x[1, 10] = bits([-(2.0 ** 50)])[0]
+    x[2, :] = bits(np.ldexp(rng.standard_normal(K), rng.integers(-60, 60, K)))
+    g, b = params(K, 989)
+    check(x, g, b, 1e-6, True)
+    check(x, g, b, 1e-6, False)
