@@ -138,7 +138,16 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
     sb = torch.empty((b_rows // 128, K // 128), dtype=torch.float32, device=dev)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     gemm_name = "fp8_gemm_grouped" if grouped else "fp8_gemm_blockscaled"
-    if grouped:
+    # small-M shapes take the split-K entry point; its workspace is allocated
+    # here, before anything is timed
+    ws_bytes = 0 if grouped else L.fp8_gemm_blockscaled_ws_bytes(M, N, K)
+    if ws_bytes:
+        gemm_name = "fp8_gemm_blockscaled_ws"
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        gemm = lambda: L.fp8_gemm_blockscaled_ws(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(),
+                                                 sb.data_ptr(), C.data_ptr(), F.FP8Q_OUT_BF16, M,
+                                                 N, K, ws.data_ptr(), ws_bytes, sp)
+    elif grouped:
         gemm = lambda: L.fp8_gemm_grouped(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(),
                                           C.data_ptr(), F.FP8Q_OUT_BF16, off_d.data_ptr(), w.G, M,
                                           N, K, sp)

@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
         L.fp8q_quant_weight_128x128.argtypes = [vp, i64, i64, vp, vp, vp]
         L.fp8_gemm_blockscaled.restype = i32
         L.fp8_gemm_blockscaled.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+        L.fp8_gemm_blockscaled_ws.restype = i32
+        L.fp8_gemm_blockscaled_ws.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+        L.fp8_gemm_blockscaled_ws_bytes.restype = i64
+        L.fp8_gemm_blockscaled_ws_bytes.argtypes = [i64, i64, i64]
         L.fp8_gemm_grouped.restype = i32
         L.fp8_gemm_grouped.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, vp]
         L.fp8q_quant_act_128x1.restype = i32
@@ -181,6 +185,34 @@ def fp8_gemm_blockscaled(a, sa, b, sb, out_dtype="bf16", c=None, stream=None):
     _check("fp8_gemm_blockscaled",
            lib().fp8_gemm_blockscaled(pa, psa, pb, psb, c.data_ptr(), code, M, N, K,
                                       _stream(stream)))
+    return c
+
+
+def fp8_gemm_blockscaled_ws(a, sa, b, sb, out_dtype="bf16", c=None, workspace=None, stream=None):
+    """fp8_gemm_blockscaled with a workspace (split-K for small-M shapes).
+    The workspace (uint8 device tensor) is allocated when not given."""
+    torch = _torch()
+    code, tdt = _out_dtype(out_dtype)
+    pa = _dev(a, "a", torch.uint8, 2)
+    psa = _dev(sa, "sa", torch.float32, 2)
+    pb = _dev(b, "b", torch.uint8, 2)
+    psb = _dev(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if K % 128 == 0 and N % 128 == 0:
+        if tuple(sa.shape) != (M, K // 128) or tuple(sb.shape) != (N // 128, K // 128):
+            raise ValueError("scale shapes must be (M, K/128) and (N/128, K/128)")
+    c = _out(c, "c", (M, N), tdt, a.device)
+    need = lib().fp8_gemm_blockscaled_ws_bytes(M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    pw = workspace.data_ptr() if workspace is not None else None
+    nw = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("fp8_gemm_blockscaled_ws",
+           lib().fp8_gemm_blockscaled_ws(pa, psa, pb, psb, c.data_ptr(), code, M, N, K, pw, nw,
+                                         _stream(stream)))
     return c
 
 

@@ -21,6 +21,10 @@ hipError_t launch_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t*
                                const float* sb, void* c, bool bf16_out, const int32_t* m_offsets,
                                int64_t G, int64_t M_total, int64_t N, int64_t K,
                                hipStream_t stream);
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const uint8_t* b,
+                                      const float* sb, void* c, bool bf16_out, int64_t M,
+                                      int64_t N, int64_t K, float* ws, hipStream_t stream);
 hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b,
                                  const float* sb_rows, void* c, bool bf16_out, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream);
@@ -159,6 +163,30 @@ int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, co
   if ((s = check_device())) return s;
   return launched(fp8q::launch_gemm_blockscaled(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16, M, N,
                                                 K, (hipStream_t)stream));
+}
+
+int64_t fp8_gemm_blockscaled_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || N % kGroup || K % kGroup) return -1;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxK) return -1;
+  return fp8q::splitk_workspace_bytes(M, N, K);
+}
+
+int fp8_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                            void* c, int out_dtype, int64_t M, int64_t N, int64_t K,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+  int s = check_gemm_common(a, sa, b, sb, c, out_dtype, M, N, K);
+  if (s == -1) return FP8Q_OK;
+  if (s) return s;
+  const int64_t need = fp8q::splitk_workspace_bytes(M, N, K);
+  if (need > 0) {
+    if (!workspace) return FP8Q_ERR_NULL;
+    if (workspace_bytes < need) return FP8Q_ERR_SHAPE;
+    if (!aligned(workspace, 16)) return FP8Q_ERR_ALIGN;
+  }
+  if ((s = check_device())) return s;
+  return launched(fp8q::launch_gemm_blockscaled_ws(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16, M, N,
+                                                   K, need > 0 ? (float*)workspace : nullptr,
+                                                   (hipStream_t)stream));
 }
 
 int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,

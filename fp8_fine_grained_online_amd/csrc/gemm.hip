@@ -548,6 +548,174 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs p) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-K small-M GEMM (with a caller workspace). The small-M kernel above
+// covers 32 columns per workgroup, so every workgroup re-reads all of A; for
+// 64 x 7168 x 7168 that is twice the bytes of B. Here a workgroup owns a
+// 64 x 128 tile (one weight block, so one B scale per group) and one of S
+// contiguous K ranges: A is read N/128 times instead of N/32, and the S
+// splits keep enough workgroups in flight. Per group the workgroup copies the
+// 64 x 128 A slab once into LDS (direct global -> LDS, two stages), its 4
+// wavefronts each stream their 32 columns of B into registers one group
+// ahead, and each wave multiplies and promotes like the small-M kernel. The
+// FP32 partial tile goes to workspace[split]; a second kernel sums the S
+// partials in split order (deterministic) and writes C.
+// (Operands, B's 128 rows included, and the A-scales all arrive by direct
+// global -> LDS copies into a ring of three stages, two groups ahead.)
+// ---------------------------------------------------------------------------
+// s_waitcnt immediate that waits for vector-memory count <= n (0..63) and
+// nothing else: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their maxima
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+constexpr int kSpM = 64;
+constexpr int kSpN = 128;
+constexpr int kSpWaves = 4;                     // one per 32 columns
+constexpr int kSpLdsA = kSpM * 128;             // A slab of one group
+constexpr int kSpLdsB = kSpN * 128;             // B slab of one group
+constexpr int kSpStage = kSpLdsA + kSpLdsB + kSpM * 4 + 64 * 4;  // + A-scales, B scale
+constexpr int kSpStages = 3;                    // copies run two groups ahead
+constexpr int kSpWorkgroups = 256;              // CUs of the chip
+constexpr int kSpCopies = 2 + 4 + 1 + 1;        // per thread per group: A, B, A-scales, B scale
+
+__global__ __launch_bounds__(64 * kSpWaves) void gemm_splitk_kernel(GemmArgs p, float* __restrict__ ws,
+                                                                    int S) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kSpStages * kSpStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lk = lane >> 4;
+  const int G = p.K / kGroup;
+  const int tiles_n = p.N / kSpN;
+  const int nb = blockIdx.x % tiles_n;
+  const int rest = blockIdx.x / tiles_n;
+  const int split = rest % S;
+  const int m0 = (rest / S) * kSpM;
+  const int n0 = nb * kSpN;
+  const int g_begin = (int)((int64_t)G * split / S);
+  const int g_end = (int)((int64_t)G * (split + 1) / S);
+
+  // Direct global -> LDS copies through buffer descriptors (rows past M read
+  // as zeros: the row part of every offset is in the range-checked per-lane
+  // offset, the group's advance in the scalar one). Slot t (16 bytes) of a
+  // slab holds row t / 8, stored chunk t % 8, i.e. global chunk
+  // (t % 8) ^ (row % 8); thread tid fills slots tid + 256 i.
+  const int rows_a = min(kSpM, p.M - m0);
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(p.a + (int64_t)m0 * p.K, (uint32_t)rows_a * (uint32_t)p.K);
+  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(p.b + (int64_t)n0 * p.K, (uint32_t)kSpN * (uint32_t)p.K);
+  const __amdgpu_buffer_rsrc_t rsrc_sa = make_rsrc(p.sa + (int64_t)m0 * G, (uint32_t)rows_a * (uint32_t)G * 4);
+  // the weight block's G scales; every lane copies the group's one scale (all
+  // 64 slots of a stage hold it), which keeps it on the copy ring: a plain
+  // load here would be a vector load whose use waits for every copy in flight
+  const __amdgpu_buffer_rsrc_t rsrc_sb = make_rsrc(p.sb + (int64_t)(n0 / kGroup) * G, (uint32_t)G * 4);
+  const int row0 = tid >> 3, lc0 = (tid & 7) ^ (row0 & 7);
+  const uint32_t off0 = (uint32_t)row0 * (uint32_t)p.K + lc0 * 16;
+  const uint32_t row_step = 32u * (uint32_t)p.K;  // slot + 256 = row + 32 (row % 8 kept)
+  const uint32_t off_sa = (uint32_t)lane * (uint32_t)G * 4;
+  auto issue = [&](int g, uint8_t* __restrict__ stage) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      load_lds(rsrc_a, stage + (i * 256 + wave * 64) * 16, 16, off0 + i * row_step, g * kGroup);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      load_lds(rsrc_b, stage + kSpLdsA + (i * 256 + wave * 64) * 16, 16, off0 + i * row_step, g * kGroup);
+    // every wave copies the same 64 A-scales to the same place: uniform counts
+    load_lds(rsrc_sa, stage + kSpLdsA + kSpLdsB, 4, off_sa, g * 4);
+    load_lds(rsrc_sb, stage + kSpLdsA + kSpLdsB + kSpM * 4, 4, 0, g * 4);
+  };
+
+  const int lane_lo = lr * 128 + ((lk ^ (lr & 7)) << 4);
+  const int lane_hi = lr * 128 + (((4 + lk) ^ (lr & 7)) << 4);
+  auto load_frag = [&](const uint8_t* blk) {
+    const uint4 lo = *(const uint4*)(blk + lane_lo);
+    const uint4 hi = *(const uint4*)(blk + lane_hi);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  v4f acc[4][2];
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Multiply the group in `st` while the copy of a later group targets `nx`;
+  // the restrict-qualified stages keep the compiler from waiting on that copy.
+  auto compute = [&](const uint8_t* __restrict__ st, uint8_t* __restrict__ nx, int g, bool copy_next) {
+    if (copy_next) issue(g + kSpStages - 1, nx);
+    const float* ssa = (const float*)(st + kSpLdsA + kSpLdsB);
+    const float sbv = ssa[kSpM];
+    v8i bfr[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) bfr[jb] = load_frag(st + kSpLdsA + (wave * 32 + jb * 16) * 128);
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      const v8i af = load_frag(st + ib * 16 * 128);
+      const float sc = ssa[ib * 16 + lr] * sbv;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const v4f pp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bfr[jb], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        acc[ib][jb][0] = __builtin_fmaf(pp[0], sc, acc[ib][jb][0]);
+        acc[ib][jb][1] = __builtin_fmaf(pp[1], sc, acc[ib][jb][1]);
+        acc[ib][jb][2] = __builtin_fmaf(pp[2], sc, acc[ib][jb][2]);
+        acc[ib][jb][3] = __builtin_fmaf(pp[3], sc, acc[ib][jb][3]);
+      }
+    }
+  };
+
+  // prologue: the first kSpStages - 1 groups
+#pragma unroll
+  for (int d = 0; d < kSpStages - 1; ++d)
+    if (g_begin + d < g_end) issue(g_begin + d, lds + d * kSpStage);
+  for (int g = g_begin; g < g_end; ++g) {
+    // this thread's copies of group g have landed once at most those of the
+    // later groups already issued (up to kSpStages - 2 of them) are
+    // outstanding: vector-memory loads complete in order
+    const int later = min(kSpStages - 2, g_end - 1 - g);
+    static_assert(kSpStages >= 2 && kSpStages <= 6, "wait table covers up to 4 later groups");
+    switch (later) {
+      case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSpCopies)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kSpCopies)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kSpCopies)); break;
+      default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * kSpCopies)); break;
+    }
+    // everyone's copies of g landed; everyone is done with g - 1. A bare
+    // barrier: __syncthreads() would also wait for the copies still in flight.
+    __builtin_amdgcn_s_barrier();
+    const int st = (g - g_begin) % kSpStages;
+    const int nx = (st + kSpStages - 1) % kSpStages;  // the stage g - 1 used
+    compute(lds + st * kSpStage, lds + nx * kSpStage, g, g + kSpStages - 1 < g_end);
+  }
+
+  // partial tile -> workspace[split][m][n] (rows past M are not stored)
+  float* wsp = ws + (int64_t)split * p.M * p.N;
+  const int nw = n0 + wave * 32;
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    const int gm = m0 + ib * 16 + lr;
+    if (gm >= p.M) continue;
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+      *(v4f*)(wsp + (int64_t)gm * p.N + nw + jb * 16 + 4 * lk) = acc[ib][jb];
+  }
+}
+
+// C = sum over the S splits, in split order, then the output rounding
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, void* c,
+                                                            int64_t n4, int64_t MN, int S) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 consecutive outputs
+  if (i >= n4) return;
+  v4f sum = *(const v4f*)(ws + 4 * i);
+  for (int s = 1; s < S; ++s) sum += *(const v4f*)(ws + (int64_t)s * MN + 4 * i);
+  if constexpr (kBf16Out) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *(bf16x4*)((__bf16*)c + 4 * i) = bf16x4{(__bf16)sum[0], (__bf16)sum[1], (__bf16)sum[2], (__bf16)sum[3]};
+  } else {
+    *(v4f*)((float*)c + 4 * i) = sum;
+  }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kGrouped, bool kRowB>
 static hipError_t launch_cfg(GemmArgs args, bool bf16_out, int m_tiles, hipStream_t stream) {
   using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N, kRowB>;
@@ -594,6 +762,43 @@ hipError_t launch_gemm_blockscaled(const uint8_t* a, const float* sa, const uint
                                    int64_t K, hipStream_t stream) {
   return launch_dense<false>(GemmArgs{a, sa, b, sb, c, nullptr, (int)M, (int)N, (int)K, 1, 0},
                              bf16_out, stream);
+}
+
+// Split-K plan for small-M shapes (those the small-M kernel would take): S
+// splits of the K groups; 0 when the shape does not take the split-K path.
+int splitk_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= kSmallTileCount || K == 0) return 0;
+  const int64_t tiles = ((M + kSpM - 1) / kSpM) * (N / kSpN);
+  const int64_t G = K / kGroup;
+  // at most one workgroup per CU: a deep copy ring leaves room for only one,
+  // and a second round of workgroups would double the time
+  int64_t S = kSpWorkgroups / tiles;
+  S = S < G ? S : G;
+  return S >= 2 ? (int)S : 0;
+}
+
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = splitk_splits(M, N, K);
+  return S ? (int64_t)S * M * N * 4 : 0;
+}
+
+hipError_t launch_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const uint8_t* b,
+                                      const float* sb, void* c, bool bf16_out, int64_t M,
+                                      int64_t N, int64_t K, float* ws, hipStream_t stream) {
+  const int S = splitk_splits(M, N, K);
+  GemmArgs args{a, sa, b, sb, c, nullptr, (int)M, (int)N, (int)K, 1, 0};
+  if (!S) return launch_dense<false>(args, bf16_out, stream);
+  const int64_t tiles = ((M + kSpM - 1) / kSpM) * (N / kSpN);
+  hipLaunchKernelGGL(gemm_splitk_kernel, dim3((unsigned)(tiles * S)), dim3(64 * kSpWaves), 0, stream,
+                     args, ws, S);
+  const int64_t n4 = M * N / 4;
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  if (bf16_out)
+    hipLaunchKernelGGL(splitk_reduce_kernel<true>, grid, dim3(256), 0, stream, ws, c, n4, M * N, S);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, stream, ws, c, n4, M * N, S);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b,

@@ -130,6 +130,33 @@ FP8Q_API int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8
                          void* c, int out_dtype, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * fp8_gemm_blockscaled with a caller workspace, for small-M shapes (few rows,
+ * e.g. 64 x 7168 x 7168). There the plain call's kernel gives every
+ * workgroup 32 columns, so every workgroup re-reads all of A; with a
+ * workspace the K groups are split across workgroups of 64 x 128 (A is read
+ * 4x less often) and the FP32 partials of the splits are summed, in split
+ * order, by a second kernel before the output rounding. Same arithmetic and
+ * the same results up to the FP32 summation order (within the tolerance of
+ * fp8_gemm_blockscaled); deterministic.
+ * Source: as fp8_gemm_blockscaled.
+ *
+ *   workspace, workspace_bytes : DEVICE scratch of at least
+ *     fp8_gemm_blockscaled_ws_bytes(M, N, K) bytes, 16-byte aligned, owned by
+ *     the caller, no contents needed on entry. When that size is 0 the shape
+ *     does not take the split path and the call is fp8_gemm_blockscaled
+ *     (workspace may then be NULL). The size is 4 * S * M * N for S splits
+ *     (S <= 256 / number of 64 x 128 tiles). Two calls in flight at once on
+ *     one workspace (different streams) race.
+ */
+FP8Q_API int fp8_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const uint8_t* b,
+                                     const float* sb, void* c, int out_dtype, int64_t M, int64_t N,
+                                     int64_t K, void* workspace, int64_t workspace_bytes,
+                                     void* stream);
+
+/* Workspace bytes fp8_gemm_blockscaled_ws needs for this shape (0: none; -1: invalid). */
+FP8Q_API int64_t fp8_gemm_blockscaled_ws_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * Grouped (MoE) block-scaled FP8 GEMM: expert e owns rows
  * [m_offsets[e], m_offsets[e+1]) of A and C and multiplies them by its own
  * weights B_e with scales sb_e, exactly as fp8_gemm_blockscaled would.

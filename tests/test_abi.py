@@ -27,7 +27,7 @@ def declared_symbols():
 ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
                 "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
                 "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1",
-                "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128"]
+                "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8_gemm_blockscaled_ws"]
 
 
 def test_header_declares_the_entry_points():
@@ -223,6 +223,21 @@ def test_dispatch_sizes_and_validation():
                 wsb=L.fp8q_moe_dispatch_workspace_bytes(0, 2, 4)) in (0, 6)
 
 
+def test_gemm_ws_validation():
+    L = _lib()
+    need = L.fp8_gemm_blockscaled_ws_bytes(64, 7168, 7168)
+    assert need > 0 and need % (64 * 7168 * 4) == 0
+    assert L.fp8_gemm_blockscaled_ws_bytes(4096, 4096, 4096) == 0  # large M: no split
+    assert L.fp8_gemm_blockscaled_ws_bytes(64, 100, 128) == -1
+    f = L.fp8_gemm_blockscaled_ws
+    W = P * 9
+    assert f(A, SA, B, SB, C, 1, 64, 7168, 7168, None, need, None) == 1
+    assert f(A, SA, B, SB, C, 1, 64, 7168, 7168, W, need - 16, None) == 2
+    assert f(A, SA, B, SB, C, 1, 64, 7168, 7168, W + 4, need, None) == 3
+    assert f(A, SA, B, SB, C, 1, 64, 100, 7168, W, need, None) == 2
+    assert f(None, None, None, None, None, 0, 0, 128, 128, None, 0, None) == 0
+
+
 def test_rowscaled_gemm_validation():
     L = _lib()
     f = L.fp8_gemm_rowscaled
@@ -246,6 +261,8 @@ def test_valid_call_without_gpu_reports_no_device():
     assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
     assert L.fp8q_quant_act_1x128_128x1(X, 128, 128, Q, SA, B, SB, None) == 6
     assert L.fp8q_norm_quant_act_1x128(X, B, None, 1e-6, 0, 4, 128, Q, SA, None) == 6
+    assert L.fp8_gemm_blockscaled_ws(A, SA, B, SB, C, 1, 64, 7168, 7168, P * 9,
+                                     L.fp8_gemm_blockscaled_ws_bytes(64, 7168, 7168), None) == 6
     assert L.fp8q_moe_dispatch_1x128(X, SB, 64, 256, 2, 4, Q, SA, 640, OFF, A, C,
                                      L.fp8q_moe_dispatch_workspace_bytes(64, 2, 4), None) == 6
     assert L.fp8q_requant_1x128_to_128x1(X, SA, 128, 128, Q, SB, None) == 6

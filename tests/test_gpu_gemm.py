@@ -216,3 +216,47 @@ def test_grouped_full_size_sampled_experts():
         if counts[e] < r1 - r0:
             pad = c[r0 + int(counts[e]):r1].float()
             assert torch.count_nonzero(pad).item() == 0
+
+
+def gpu_pipeline_ws(a_bits, b_bits, out):
+    """As gpu_pipeline, through fp8_gemm_blockscaled_ws (split-K for small M)."""
+    import fp8_fine_grained_online_amd as F
+    import torch
+    qa, sa = F.fp8q_quant_act_1x128(to_dev_bf16(a_bits))
+    qb, sb = F.fp8q_quant_weight_128x128(to_dev_bf16(b_bits))
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    c = poisoned((a_bits.shape[0], b_bits.shape[0]), dt)
+    F.fp8_gemm_blockscaled_ws(qa, sa, qb, sb, out, c=c)
+    torch.cuda.synchronize()
+    return from_dev_bf16_bits(c) if out == "bf16" else c.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 256), (64, 1024, 2048), (100, 2048, 1024),
+                                   (128, 4096, 512), (200, 384, 4096), (64, 256, 128)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_split_k_workspace_path(M, N, K, out):
+    import fp8_fine_grained_online_amd as F
+    assert F.lib().fp8_gemm_blockscaled_ws_bytes(M, N, K) > 0 or K == 128  # the split path runs
+    a = S.activations(M, K, S.rng_for(870 + M, N))
+    b = S.weights(N, K, S.rng_for(870 + M, N + 1))
+    c64, S_, T = oracle_rows(a, b)
+    check(gpu_pipeline_ws(a, b, out), c64, S_, T, out)
+
+
+def test_split_k_full_size_64x7168x7168_sampled_columns():
+    """The small-M workload in the launch configuration the bench times; all 64
+    rows on 512 sampled columns (the truncation bound on those columns only)."""
+    from oracle import gemm, quant
+    w = S.WORKLOADS["skinny_64x7168x7168"]
+    a, b = S.dense_inputs(w)
+    got = gpu_pipeline_ws(a, b, "bf16")
+    cols = np.sort(S.rng_for(871, 0).choice(w.N, 512, replace=False))
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant.quant_weight_128x128(b)
+    sb_rows = np.repeat(sb, 128, axis=0)[cols]
+    c64 = gemm.gemm_rowscaled_f64(qa, sa, qb[cols], sb_rows)
+    S_ = gemm.abs_sum_rowscaled(qa, sa, qb[cols], sb_rows)
+    T = mfma_bound(qa, sa, qb[cols], sb_rows, row_scales=True)
+    from oracle import bf16
+    want = gemm.round_bf16(c64)
+    check_bf16(got[:, cols], c64, S_, T, want, bf16.ulp(want))
