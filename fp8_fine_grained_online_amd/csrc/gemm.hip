@@ -355,23 +355,54 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     sbv = sbv_next;
   }
 
-  // ---- epilogue: each lane stores 4 consecutive columns of one row ----
+  // ---- epilogue ----
+  if constexpr (kBf16Out) {
+    // The MFMA layout gives a lane 4 columns (8 bytes) of one row, so direct
+    // stores would write every 128-byte line in four 32-byte pieces. Instead
+    // each wave stages its WM x WN tile in its own part of the (now idle) LDS
+    // and stores whole 128-byte row segments, 16 bytes per lane. LDS rows are
+    // 128 bytes with the 16-byte chunk index XOR row % 8, so the staging
+    // writes of 16 rows hit distinct banks pairwise and the reads are
+    // conflict-free. The loop above ends with a barrier, so no wave still
+    // reads the stages.
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    static_assert(WN * 2 == 128, "one 128-byte row segment per wave row");
+    static_assert(WAVES_M * WAVES_N * WM * 128 <= Cfg::kLdsBytes, "staging fits in the stages");
+    uint8_t* tile = lds + wave * (WM * 128);
 #pragma unroll
-  for (int i = 0; i < SUBM; ++i) {
-    const int gm = m0 + wm * WM + i * 16 + lr;
-    if (gm >= m_end) continue;
+    for (int i = 0; i < SUBM; ++i) {
+      const int m = i * 16 + lr;
 #pragma unroll
-    for (int j = 0; j < SUBN; ++j) {
-      const int gn = n0 + wn * WN + j * 16 + 4 * lk;
-      if (gn >= p.N) continue;  // N % 128 == 0: a group of 4 columns is all in or all out
-      const int64_t off = (int64_t)gm * p.N + gn;
-      if constexpr (kBf16Out) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      for (int j = 0; j < SUBN; ++j) {
+        const int byte = j * 32 + lk * 8;  // column (j * 16 + 4 * lk) * 2 bytes
         const bf16x4 v = {(__bf16)acc[i][j][0], (__bf16)acc[i][j][1], (__bf16)acc[i][j][2],
                           (__bf16)acc[i][j][3]};
-        *(bf16x4*)((__bf16*)p.c + off) = v;
-      } else {
-        *(v4f*)((float*)p.c + off) = acc[i][j];
+        *(bf16x4*)(tile + m * 128 + ((((byte >> 4) ^ (m & 7))) << 4) + (byte & 15)) = v;
+      }
+    }
+    __syncthreads();
+    const int nw = n0 + wn * WN;  // N % 128 == 0: the wave's 64 columns are all in or all out
+    if (nw < p.N) {
+      const int c = lane & 7;
+#pragma unroll
+      for (int k = 0; k < WM / 8; ++k) {
+        const int m = k * 8 + (lane >> 3);
+        const int gm = m0 + wm * WM + m;
+        const uint4 v = *(const uint4*)(tile + m * 128 + ((c ^ (m & 7)) << 4));
+        if (gm < m_end) *(uint4*)((__bf16*)p.c + (int64_t)gm * p.N + nw + c * 8) = v;
+      }
+    }
+  } else {
+    // each lane stores 4 consecutive FP32 columns (16 bytes) of one row
+#pragma unroll
+    for (int i = 0; i < SUBM; ++i) {
+      const int gm = m0 + wm * WM + i * 16 + lr;
+      if (gm >= m_end) continue;
+#pragma unroll
+      for (int j = 0; j < SUBN; ++j) {
+        const int gn = n0 + wn * WN + j * 16 + 4 * lk;
+        if (gn >= p.N) continue;  // N % 128 == 0: a group of 4 columns is all in or all out
+        *(v4f*)((float*)p.c + (int64_t)gm * p.N + gn) = acc[i][j];
       }
     }
   }
