@@ -393,16 +393,32 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
       }
     }
   } else {
-    // each lane stores 4 consecutive FP32 columns (16 bytes) of one row
+    // FP32: the same staging in two passes of WM / 2 rows (a row is 256
+    // bytes, 16 chunks of 16 bytes at chunk index XOR row % 16)
+    static_assert(WN * 4 == 256 && SUBM % 2 == 0, "two passes of 256-byte rows");
+    static_assert(WAVES_M * WAVES_N * (WM / 2) * 256 <= Cfg::kLdsBytes, "staging fits in the stages");
+    uint8_t* tile = lds + wave * ((WM / 2) * 256);
+    const int nw = n0 + wn * WN;
+    const int c = lane & 15;
 #pragma unroll
-    for (int i = 0; i < SUBM; ++i) {
-      const int gm = m0 + wm * WM + i * 16 + lr;
-      if (gm >= m_end) continue;
+    for (int h = 0; h < 2; ++h) {
+      if (h) __syncthreads();  // the first pass's reads are done before the tile is rewritten
 #pragma unroll
-      for (int j = 0; j < SUBN; ++j) {
-        const int gn = n0 + wn * WN + j * 16 + 4 * lk;
-        if (gn >= p.N) continue;  // N % 128 == 0: a group of 4 columns is all in or all out
-        *(v4f*)((float*)p.c + (int64_t)gm * p.N + gn) = acc[i][j];
+      for (int i = 0; i < SUBM / 2; ++i) {
+        const int m = i * 16 + lr;
+#pragma unroll
+        for (int j = 0; j < SUBN; ++j)
+          *(v4f*)(tile + m * 256 + (((j * 4 + lk) ^ (m & 15)) << 4)) = acc[h * (SUBM / 2) + i][j];
+      }
+      __syncthreads();
+      if (nw < p.N) {
+#pragma unroll
+        for (int k = 0; k < WM / 8; ++k) {
+          const int m = k * 4 + (lane >> 4);
+          const int gm = m0 + wm * WM + h * (WM / 2) + m;
+          const v4f v = *(const v4f*)(tile + m * 256 + ((c ^ (m & 15)) << 4));
+          if (gm < m_end) *(v4f*)((float*)p.c + (int64_t)gm * p.N + nw + c * 4) = v;
+        }
       }
     }
   }
@@ -779,13 +795,7 @@ static hipError_t launch_dense(GemmArgs args, bool bf16_out, hipStream_t stream)
       hipLaunchKernelGGL((gemm_skinny_kernel<false, kRowB>), grid, dim3(64 * kSkWaves), 0, stream, args);
     return hipGetLastError();
   }
-  // Row-scaled B holds WN/4 column scales per lane through a step; a 64x64
-  // wave tile (256 x 128 workgroup tile) keeps that within the registers of
-  // two waves per SIMD.
-  if constexpr (kRowB)
-    return launch_cfg<256, 128, 4, 2, false, true>(args, bf16_out, (int)((M + 255) / 256), stream);
-  else
-    return launch_cfg<256, 256, 2, 4, false, false>(args, bf16_out, (int)((M + 255) / 256), stream);
+  return launch_cfg<256, 256, 2, 4, false, kRowB>(args, bf16_out, (int)((M + 255) / 256), stream);
 }
 
 hipError_t launch_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
