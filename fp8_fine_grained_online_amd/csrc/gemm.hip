@@ -336,6 +336,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     }
   };
 
+  // A wave whose 16-row blocks all lie past the tile's valid rows (the
+  // 128-row remainder of an expert, a ragged last row tile) only copies its
+  // share of each group and keeps the barriers; its MFMAs would multiply the
+  // zero rows. The other wave of its SIMD then has the matrix core alone.
+  const bool idle = wm * WM >= rows_a;
+
   // ---- main loop: group g computes from stage g % 2 while g+1 streams into the other ----
   float sbv = 0.0f;
   if (G > 0) {
@@ -349,7 +355,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     uint8_t* nxt = lds + ((g + 1) & 1) * Cfg::kStage;
     const float sbv_next = (!kRowB && g + 1 < G) ? gsb[g + 1] : 0.0f;
     // the last group re-copies itself into the idle stage (never read): no branch in the step
-    step(cur, nxt, min(g + 1, G - 1), sbv);
+    if (idle)
+      issue_loads(min(g + 1, G - 1), nxt);
+    else
+      step(cur, nxt, min(g + 1, G - 1), sbv);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this thread's copies have landed
     __syncthreads();                     // ... and everyone's; `cur` is free again
     sbv = sbv_next;
