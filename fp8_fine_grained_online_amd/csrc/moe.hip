@@ -10,7 +10,7 @@
 // multiples of 128, padding rows zero).
 //
 // Row order inside an expert's block is slot order, slot = token * k + choice,
-// so the layout is deterministic. Five launches:
+// so the layout is deterministic. Four launches:
 //   count  per 256-slot block, a histogram of the valid choices (LDS atomics);
 //   scan   one workgroup, 1024/G threads per expert: per-expert totals, padded
 //          offsets, and for every (block, expert) the first row that block's
@@ -19,8 +19,8 @@
 //          (one ballot per distinct expert present), the 4 wavefronts' counts
 //          are added in LDS, and row = base + earlier waves + rank;
 //   quant  one wavefront per token: read and quantize the token once, store
-//          its codes and scales to each of its rows;
-//   pad    one workgroup per possible padding row (127 per expert): zero it.
+//          its codes and scales to each of its rows; further wavefronts, one
+//          per possible padding row (127 per expert), zero the padding rows.
 #include "common.hpp"
 
 namespace fp8q {
@@ -44,19 +44,20 @@ __global__ __launch_bounds__(kDispBlock) void dispatch_count_kernel(const int32_
   for (int e = threadIdx.x; e < G; e += kDispBlock) hist[(int64_t)blockIdx.x * G + e] = h[e];
 }
 
-// One workgroup. Thread (e, p) = (tid / tpe, tid % tpe), tpe = 1024 / G
+// One workgroup. Thread (e, p) = (tid % G, tid / G), p < tpe = 1024 / G
 // threads per expert, owns the contiguous run of blocks [p * chunk, (p+1) *
 // chunk) of expert e's column of the histogram: it sums them, the partial sums
 // of an expert are combined in LDS (totals, then a prefix over p), and the
-// thread writes the base row of each of its blocks.
+// thread writes the base row of each of its blocks. Neighbouring threads take
+// neighbouring experts, so each histogram row is read and written coalesced.
 __global__ __launch_bounds__(kMaxExperts) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int n_blk, int G, int32_t* __restrict__ base,
     int32_t* __restrict__ counts, int32_t* __restrict__ m_offsets) {
   __shared__ int32_t part[kMaxExperts];  // [e * tpe + p]
   __shared__ int32_t off[kMaxExperts + 1];
   const int tpe = kMaxExperts / G;
-  const int e = threadIdx.x / tpe, p = threadIdx.x % tpe;
-  const bool on = e < G;
+  const int e = threadIdx.x % G, p = threadIdx.x / G;
+  const bool on = p < tpe;
   const int chunk = (n_blk + tpe - 1) / tpe;
   const int b0 = min(p * chunk, n_blk), b1 = min(b0 + chunk, n_blk);
   int sum = 0;
@@ -143,32 +144,53 @@ __global__ __launch_bounds__(kDispBlock) void dispatch_rank_kernel(const int32_t
 // One wavefront per token. Lane l owns 16 consecutive values (32 bytes in, 16
 // bytes of codes out) of each 1024-value step, so a 1x128 tile is 8 lanes
 // (half a DPP row) and every destination row gets one 16-byte store per lane
-// and one 32-byte run of 8 scales per step.
+// per step. The scales are gathered across steps, one lane shuffle per step,
+// until lane l holds the scale of tile 64 w + l of window w (8 steps); each
+// destination row then gets the window's scales in one contiguous store.
+//
+// Wavefronts past the T tokens zero the padding rows: wavefront T + 127 e + i
+// takes row m_offsets[e] + counts[e] + i when that row is below m_offsets[e+1].
 __global__ __launch_bounds__(256) void dispatch_quant_kernel(const uint4* __restrict__ x, int T,
                                                              int K, int k,
                                                              const int32_t* __restrict__ row_of_slot,
-                                                             uint2* __restrict__ q,
+                                                             const int32_t* __restrict__ m_offsets,
+                                                             const int32_t* __restrict__ counts,
+                                                             int n_experts, uint2* __restrict__ q,
                                                              float* __restrict__ sa) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (t >= T) return;
   const int n_chunks = K / 8;
   const int G = K / kGroup;
+  if (t >= T) {
+    const int pi = t - T;
+    const int e = pi / (kGroup - 1);
+    if (e >= n_experts) return;
+    const int64_t row = (int64_t)m_offsets[e] + counts[e] + pi % (kGroup - 1);
+    if (row >= m_offsets[e + 1]) return;  // at most 127 padding rows per expert
+    uint4* qr = (uint4*)q + row * (K / 16);
+    for (int c = lane; c < K / 16; c += 64) qr[c] = make_uint4(0, 0, 0, 0);
+    for (int c = lane; c < G; c += 64) sa[row * G + c] = 0.0f;
+    return;
+  }
   const uint4* xr = x + (int64_t)t * n_chunks;
   const int32_t* rows = row_of_slot + (int64_t)t * k;
+  const int n_steps = (n_chunks + 127) / 128;
+  float win = 0.0f;          // this lane's tile of the current window, once gathered
   constexpr int kBatch = 2;  // steps whose loads are in flight together
-  for (int p0 = 0; p0 < n_chunks; p0 += 128 * kBatch) {
+  for (int s0 = 0; s0 < n_steps; s0 += kBatch) {
     uint4 v[kBatch][2];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int c = p0 + 128 * u + 2 * lane;  // this lane's first chunk
-      const bool have = c < n_chunks;         // whole tiles (8 lanes) are present or absent
+      const int c = (s0 + u) * 128 + 2 * lane;  // this lane's first chunk
+      const bool have = c < n_chunks;           // whole tiles (8 lanes) are present or absent
       v[u][0] = have ? load_nt(xr + c) : make_uint4(0, 0, 0, 0);
       v[u][1] = have ? load_nt(xr + c + 1) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int c = p0 + 128 * u + 2 * lane;
+      const int st = s0 + u;
+      if (st >= n_steps) break;  // wave-uniform
+      const int c = st * 128 + 2 * lane;
       const bool have = c < n_chunks;
       const float m = fmaxf(absmax8(v[u][0]), absmax8(v[u][1]));
       const float amax = __uint_as_float(row8_max_u32(__float_as_uint(m)));
@@ -181,25 +203,24 @@ __global__ __launch_bounds__(256) void dispatch_quant_kernel(const uint4* __rest
           const int row = rows[j];  // same for the whole wavefront
           if (row < 0) continue;   // dropped choice
           *(uint4*)(q + ((int64_t)row * n_chunks + c)) = codes;
-          if ((lane & 7) == 0) sa[(int64_t)row * G + (c >> 4)] = s;
+        }
+      }
+      // at step st, lane l with l / 8 == st % 8 takes the scale of tile
+      // 8 st + l % 8, which lanes 8 (l % 8) .. 8 (l % 8) + 7 hold
+      const float got = __shfl(s, (lane & 7) * 8);
+      if ((lane >> 3) == (st & 7)) win = got;
+      if ((st & 7) == 7 || st == n_steps - 1) {
+        const int tile = (st & ~7) * 8 + lane;  // window st / 8 covers tiles 64 (st / 8) + 0..63
+        if (tile < G) {
+          for (int j = 0; j < k; ++j) {
+            const int row = rows[j];
+            if (row < 0) continue;
+            sa[(int64_t)row * G + tile] = win;
+          }
         }
       }
     }
   }
-}
-
-// grid (127, G): workgroup (i, e) zeroes padding row i of expert e, if it exists
-__global__ __launch_bounds__(256) void dispatch_pad_kernel(const int32_t* __restrict__ m_offsets,
-                                                           const int32_t* __restrict__ counts,
-                                                           int K, uint4* __restrict__ q,
-                                                           float* __restrict__ sa) {
-  const int e = blockIdx.y;
-  const int64_t row = (int64_t)m_offsets[e] + counts[e] + blockIdx.x;
-  if (row >= m_offsets[e + 1]) return;  // at most 127 padding rows per expert
-  const int n16 = K / 16;
-  for (int i = threadIdx.x; i < n16; i += 256) q[row * n16 + i] = make_uint4(0, 0, 0, 0);
-  const int G = K / kGroup;
-  for (int i = threadIdx.x; i < G; i += 256) sa[row * G + i] = 0.0f;
 }
 
 int64_t dispatch_blocks(int64_t slots) { return (slots + kDispBlock - 1) / kDispBlock; }
@@ -225,11 +246,11 @@ hipError_t launch_moe_dispatch(const void* x, const int32_t* ids, int64_t T, int
     hipLaunchKernelGGL(dispatch_rank_kernel, dim3((unsigned)n_blk), dim3(kDispBlock), 0, stream, ids,
                        (int)S, (int)G, base, row_of_slot);
   if (K > 0) {
-    if (T > 0)
-      hipLaunchKernelGGL(dispatch_quant_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
-                         (const uint4*)x, (int)T, (int)K, (int)k, row_of_slot, (uint2*)q, sa);
-    hipLaunchKernelGGL(dispatch_pad_kernel, dim3(kGroup - 1, (unsigned)G), dim3(256), 0, stream,
-                       m_offsets, counts, (int)K, (uint4*)q, sa);
+    // the tokens' wavefronts, then one per possible padding row
+    const int64_t waves = T + (kGroup - 1) * G;
+    hipLaunchKernelGGL(dispatch_quant_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
+                       (const uint4*)x, (int)T, (int)K, (int)k, row_of_slot, m_offsets, counts,
+                       (int)G, (uint2*)q, sa);
   }
   return hipGetLastError();
 }
