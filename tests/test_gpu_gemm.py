@@ -243,6 +243,28 @@ def test_split_k_workspace_path(M, N, K, out):
     check(gpu_pipeline_ws(a, b, out), c64, S_, T, out)
 
 
+def test_split_k_workspace_reuse_across_calls_and_shapes():
+    """One workspace serves calls of different shapes in a row: every call's
+    output is bit-identical to a call on a fresh workspace (the summation order
+    over the splits is fixed)."""
+    import fp8_fine_grained_online_amd as F
+    import torch
+    shapes = [(64, 1024, 2048), (48, 512, 1024), (64, 1024, 2048), (130, 256, 4096)]
+    need = max(F.lib().fp8_gemm_blockscaled_ws_bytes(M, N, K) for M, N, K in shapes)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")  # no contents needed
+    for i, (M, N, K) in enumerate(shapes):
+        a = S.activations(M, K, S.rng_for(873, i))
+        b = S.weights(N, K, S.rng_for(874, i))
+        qa, sa = F.fp8q_quant_act_1x128(to_dev_bf16(a))
+        qb, sb = F.fp8q_quant_weight_128x128(to_dev_bf16(b))
+        fresh = F.fp8_gemm_blockscaled_ws(qa, sa, qb, sb, "f32",
+                                          c=poisoned((M, N), torch.float32))
+        reused = F.fp8_gemm_blockscaled_ws(qa, sa, qb, sb, "f32",
+                                           c=poisoned((M, N), torch.float32), workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(fresh.view(torch.int32), reused.view(torch.int32)), (M, N, K)
+
+
 def test_split_k_full_size_64x7168x7168_sampled_columns():
     """The small-M workload in the launch configuration the bench times; all 64
     rows on 512 sampled columns (the truncation bound on those columns only)."""
