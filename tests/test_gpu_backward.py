@@ -229,12 +229,15 @@ def test_rowscaled_small_and_ragged(M, N, K, out):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_rowscaled_big_tile_path_ragged_m(out):
-    """Enough tiles for the large-tile kernel (M = 2000 is ragged against 256);
-    sampled rows including the last tile's."""
-    M, N, K = 2000, 4224, 512
+@pytest.mark.parametrize("M", [2000, 1900])
+def test_rowscaled_big_tile_path_ragged_m(M, out):
+    """Enough tiles for the large-tile kernel, M ragged against 256; sampled
+    rows including the last tile's. With M = 1900 the last row tile has 108
+    rows, so the waves of its upper 128 rows only copy (no MFMAs)."""
+    N, K = 4224, 512
     qa, sa, qb, sb = rowscaled_operands(M, N, K, 951)
-    rows = np.concatenate([np.arange(0, 16), np.arange(1000, 1008), np.arange(1984, 2000)])
+    rows = np.concatenate([np.arange(0, 16), np.arange(1000, 1008), np.arange(1780, 1800),
+                           np.arange(M - 16, M)])
     got = gpu_rowscaled(qa, sa, qb, sb, out, rows)
     check_rowscaled(got, qa[rows], sa[rows], qb, sb, out)
 

@@ -73,13 +73,16 @@ def test_ragged_shapes(M, N, K, out):
     check(gpu_pipeline(a, b, out), c64, S_, T, out)
 
 
-def test_big_tile_path_ragged_m_and_n():
+@pytest.mark.parametrize("M", [2000, 1900])
+def test_big_tile_path_ragged_m_and_n(M):
     """Enough 256x256 tiles for the large-tile kernel, with M and N both ragged
-    against 256 (M = 2000, N = 4224 = 33 x 128); sampled rows incl. the tail."""
-    M, N, K = 2000, 4224, 512
+    against 256 (N = 4224 = 33 x 128); sampled rows incl. the tail. With
+    M = 1900 the last row tile has 108 rows: the waves of its upper 128 rows
+    only copy (no MFMAs)."""
+    N, K = 4224, 512
     a = S.activations(M, K, S.rng_for(860, 0))
     b = S.weights(N, K, S.rng_for(860, 1))
-    rows = np.unique(np.concatenate([[0, 255, 256, 1791, 1792, 1999],
+    rows = np.unique(np.concatenate([[0, 255, 256, 1791, 1792, 1890, M - 1],
                                      S.rng_for(860, 2).integers(0, M, 20)]))
     for out in ["f32", "bf16"]:
         got = gpu_pipeline(a, b, out, rows=rows)
