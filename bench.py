@@ -93,6 +93,32 @@ def cpu_baseline(workload, a_bits, b_bits, rows):
     }
 
 
+def cpu_baseline_grouped(workload, a_bits, b_bits, off, counts, budget_s=10.0):
+    """The oracle, untuned, on the real rows of experts 0, 1, ... until about
+    `budget_s` seconds of CPU work (at least one expert)."""
+    from oracle import gemm, quant
+    threads = oracle_threads()
+    N, K = b_bits.shape[1:]
+    t0 = time.perf_counter()
+    e, rows = 0, 0
+    while e < len(counts) and (e == 0 or time.perf_counter() - t0 < budget_s):
+        r0, n = int(off[e]), int(counts[e])
+        qa, sa = quant.quant_act_1x128(a_bits[r0:r0 + n])
+        qb, sb = quant.quant_weight_128x128(b_bits[e])
+        gemm.round_bf16(gemm.gemm_blockscaled_f64(qa, sa, qb, sb))
+        e, rows = e + 1, rows + n
+    dt = time.perf_counter() - t0
+    return {
+        "value": 2.0 * rows * N * K / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{workload}: oracle quantization of the real rows of experts 0..{e - 1} "
+                   f"({rows} rows) and of their weights ({N}x{K} each), float64 per-group GEMM, "
+                   f"bf16 rounding; {dt:.2f} s"),
+    }
+
+
 def copy_calibration(steps, warmup):
     """A plain 512 MiB device-to-device copy: bytes moved are known exactly."""
     import torch
@@ -167,10 +193,8 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
 
     def cpu():
         if grouped:
-            r0 = int(off[0])
-            n0 = int(off[1] - off[0])
-            return cpu_baseline(args.workload + " expert 0", a_bits[r0:r0 + n0], b_bits[0], n0)
-        return cpu_baseline(args.workload, a_bits, b_bits, min(M, 4096))
+            return cpu_baseline_grouped(args.workload, a_bits, b_bits, off, counts)
+        return cpu_baseline(args.workload, a_bits, b_bits, M)  # the whole workload
 
     # algorithmic bytes of the GEMM: operands, scales and output, each once
     gemm_bytes = (M * K + b_rows * K + M * (K // 128) * 4 + (b_rows // 128) * (K // 128) * 4
@@ -243,7 +267,7 @@ def plan_backward(w, args, F, S, L, dev, sp, up_bf16):
                            "fp8_gemm_blockscaled) + Wgrad (requant_1x128_to_128x1(X) + "
                            "fp8_gemm_rowscaled)"},
         "extra": {},
-        "cpu": lambda: cpu_baseline_backward(args.workload, x_bits, w_bits, dy_bits, 64),
+        "cpu": lambda: cpu_baseline_backward(args.workload, x_bits, w_bits, dy_bits, 256),
     }
 
 
@@ -265,11 +289,11 @@ def plan_stream(w, args, F, S, L, dev, sp, up_bf16):
         fn = lambda: L.fp8q_norm_quant_act_1x128(X.data_ptr(), g.data_ptr(), None, 1e-6, 0, M, K,
                                                  q.data_ptr(), sa.data_ptr(), sp)
         nbytes += 2 * K
-        cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, 256, g_bits)
+        cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, M, g_bits)
     else:
         name = "quant_act_1x128"
         fn = lambda: L.fp8q_quant_act_1x128(X.data_ptr(), M, K, q.data_ptr(), sa.data_ptr(), sp)
-        cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, 2048, None)
+        cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, M, None)
     return {
         "launches": [(name, fn)],
         "flops": {},
@@ -310,7 +334,7 @@ def plan_dispatch(w, args, F, S, L, dev, sp, up_bf16):
     if not w.N:
         return {"launches": launches, "flops": {}, "bytes": {"moe_dispatch_1x128": nbytes},
                 "stream": "moe_dispatch_1x128", "config": config, "extra": {},
-                "cpu": lambda: cpu_baseline_dispatch(args.workload, x_bits, ids, G, 256)}
+                "cpu": lambda: cpu_baseline_dispatch(args.workload, x_bits, ids, G, T)}
     N = w.N
     B = up_bf16(b_bits)
     qb = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
@@ -331,7 +355,7 @@ def plan_dispatch(w, args, F, S, L, dev, sp, up_bf16):
             "bytes": {"moe_dispatch_1x128": nbytes,
                       "quant_weight_128x128": G * N * K * 3 + (G * N // 128) * (K // 128) * 4},
             "config": config, "extra": {},
-            "cpu": lambda: cpu_baseline(args.workload + " expert 0", x_bits[:128], b_bits[0], 128)}
+            "cpu": lambda: cpu_baseline(args.workload + " expert 0", x_bits[:2048], b_bits[0], 2048)}
 
 
 def cpu_baseline_dispatch(workload, x_bits, ids, G, tokens):
