@@ -41,10 +41,16 @@ STREAM_SOURCES = {"quant_act_1x128": ("quant.hip", "common.hpp"),
 
 
 def source_hash(*names):
+    """Hash of the kernel sources with comments and whitespace removed, so that
+    recorded counters stay valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "fp8_fine_grained_online_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "fp8_fine_grained_online_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   static_assert(!(kGrouped && kRowB), "row-scaled B is dense only");
   constexpr int WM = Cfg::kWM, WN = Cfg::kWN;
   constexpr int SUBM = Cfg::kSubM, SUBN = Cfg::kSubN;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg::kLdsBytes];  // two stages
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg::kLdsBytes];  // two stages; the epilogue's staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -610,14 +610,13 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_skinny_kernel(GemmArgs p) 
 // 64 x 7168 x 7168 that is twice the bytes of B. Here a workgroup owns a
 // 64 x 128 tile (one weight block, so one B scale per group) and one of S
 // contiguous K ranges: A is read N/128 times instead of N/32, and the S
-// splits keep enough workgroups in flight. Per group the workgroup copies the
-// 64 x 128 A slab once into LDS (direct global -> LDS, two stages), its 4
-// wavefronts each stream their 32 columns of B into registers one group
-// ahead, and each wave multiplies and promotes like the small-M kernel. The
-// FP32 partial tile goes to workspace[split]; a second kernel sums the S
-// partials in split order (deterministic) and writes C.
-// (Operands, B's 128 rows included, and the A-scales all arrive by direct
-// global -> LDS copies into a ring of three stages, two groups ahead.)
+// splits give about one workgroup per CU (never more, see splitk_splits).
+// Per group the workgroup's A slab (64 x 128), B slab (128 x 128), the 64
+// A-scales and the B scale all arrive by direct global -> LDS copies into a
+// ring of three stages, two groups ahead; each of the 4 wavefronts multiplies
+// its 32 columns and promotes like the large-tile kernel. The FP32 partial
+// tile goes to workspace[split]; a second kernel sums the S partials in split
+// order (deterministic) and writes C.
 // ---------------------------------------------------------------------------
 // s_waitcnt immediate that waits for vector-memory count <= n (0..63) and
 // nothing else: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their maxima
