@@ -173,8 +173,15 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
     gemm_name = "fp8_gemm_grouped" if grouped else "fp8_gemm_blockscaled"
     # small-M shapes take the split-K entry point; its workspace is allocated
     # here, before anything is timed
-    ws_bytes = 0 if grouped else L.fp8_gemm_blockscaled_ws_bytes(M, N, K)
-    if ws_bytes:
+    ws_bytes = 0 if grouped or w.quant_on_load else L.fp8_gemm_blockscaled_ws_bytes(M, N, K)
+    if w.quant_on_load:
+        # A is quantized inside the GEMM (its codes and scales are stored too,
+        # as the activation quantizer would store them for the backward pass)
+        gemm_name = "fp8_gemm_blockscaled_bf16a"
+        gemm = lambda: L.fp8_gemm_blockscaled_bf16a(A.data_ptr(), qb.data_ptr(), sb.data_ptr(),
+                                                    C.data_ptr(), F.FP8Q_OUT_BF16, M, N, K,
+                                                    qa.data_ptr(), sa.data_ptr(), sp)
+    elif ws_bytes:
         gemm_name = "fp8_gemm_blockscaled_ws"
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         gemm = lambda: L.fp8_gemm_blockscaled_ws(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(),
@@ -196,6 +203,8 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
                                              sp)),
         (gemm_name, gemm),
     ]
+    if w.quant_on_load:
+        launches = launches[1:]
 
     def cpu():
         if grouped:
@@ -205,16 +214,20 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
     # algorithmic bytes of the GEMM: operands, scales and output, each once
     gemm_bytes = (M * K + b_rows * K + M * (K // 128) * 4 + (b_rows // 128) * (K // 128) * 4
                   + 2 * M * N)
+    if w.quant_on_load:
+        gemm_bytes += 2 * M * K  # A read in bf16 (2 B, not 1) and its codes written
     return {
         "launches": launches,
         "flops": {gemm_name: flops},
         "flops_step": flops,
         "gemm_bytes": {gemm_name: gemm_bytes},
-        "bytes": {"quant_act_1x128": M * K * 3 + M * (K // 128) * 4,
-                  "quant_weight_128x128": b_rows * K * 3 + (b_rows // 128) * (K // 128) * 4},
+        "bytes": {n: b for n, b in (("quant_act_1x128", M * K * 3 + M * (K // 128) * 4),
+                                    ("quant_weight_128x128",
+                                     b_rows * K * 3 + (b_rows // 128) * (K // 128) * 4))
+                  if n in [name for name, _ in launches]},
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "G": w.G or None,
                    "tokens": w.tokens or None, "out": "bf16",
-                   "step": "quant_act_1x128 + quant_weight_128x128 + " + gemm_name},
+                   "step": " + ".join(name for name, _ in launches)},
         "extra": {"gemm_tflops_padded": (gemm_name, 2.0 * M * N * K)},
         "cpu": cpu,
     }
@@ -555,7 +568,9 @@ def main():
         gemm_tflops = plan["flops"][gemm_name] / (kms[gemm_name] * 1e-3) / 1e12
         metric = METRIC
         value, unit = plan["flops_step"] / (ms_step * 1e-3) / 1e12, "TFLOP/s"
-        traffic = measured_traffic(args.workload, ("gemm.hip", "common.hpp"))
+        gemm_src = ("gemm_qa.hip" if gemm_name == "fp8_gemm_blockscaled_bf16a" else "gemm.hip",
+                    "tiles.hpp", "common.hpp")
+        traffic = measured_traffic(args.workload, gemm_src)
         gbytes = plan.get("gemm_bytes", {}).get(gemm_name)
         ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         if gbytes and plan["flops"][gemm_name] / gbytes < ridge:

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   fp8q_quant_weight_128x128(w)               -> (q, sb)
   fp8_gemm_blockscaled(a, sa, b, sb, out_dtype)          -> c
   fp8_gemm_blockscaled_ws(a, sa, b, sb, out_dtype)       -> c   (split-K for small M)
+  fp8_gemm_blockscaled_bf16a(a_bf16, b, sb, out_dtype)   -> c [, qa, sa]   quantize-on-load
   fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype)   -> c
   fp8q_norm_quant_act_1x128(x, gamma, eps, beta, centred) -> (q, sa)   normalization + cast
   fp8q_moe_dispatch_1x128(x, topk_ids, G) -> (q, sa, m_offsets, row_of_slot)   MoE FP8 dispatch
@@ -29,6 +30,7 @@ from ._lib import (  # noqa: F401
     FP8Q_OUT_F32,
     STATUS,
     fp8_gemm_blockscaled,
+    fp8_gemm_blockscaled_bf16a,
     fp8_gemm_blockscaled_ws,
     fp8_gemm_grouped,
     fp8_gemm_rowscaled,
@@ -48,7 +50,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Fp8qError", "FP8Q_OUT_BF16", "FP8Q_OUT_F32", "STATUS",
     "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
-    "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_ws", "fp8_gemm_grouped", "fp8q_version", "lib", "lib_path",
+    "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_bf16a", "fp8_gemm_blockscaled_ws", "fp8_gemm_grouped", "fp8q_version", "lib", "lib_path",
     "fp8q_quant_act_128x1", "fp8q_quant_act_1x128_128x1", "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8q_requant_1x128_to_128x1", "fp8q_transpose_weight_128x128",
     "fp8_gemm_rowscaled",
 ]

@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L.fp8q_quant_weight_128x128.argtypes = [vp, i64, i64, vp, vp, vp]
         L.fp8_gemm_blockscaled.restype = i32
         L.fp8_gemm_blockscaled.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+        L.fp8_gemm_blockscaled_bf16a.restype = i32
+        L.fp8_gemm_blockscaled_bf16a.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, vp]
         L.fp8_gemm_blockscaled_ws.restype = i32
         L.fp8_gemm_blockscaled_ws.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
         L.fp8_gemm_blockscaled_ws_bytes.restype = i64
@@ -186,6 +188,34 @@ def fp8_gemm_blockscaled(a, sa, b, sb, out_dtype="bf16", c=None, stream=None):
            lib().fp8_gemm_blockscaled(pa, psa, pb, psb, c.data_ptr(), code, M, N, K,
                                       _stream(stream)))
     return c
+
+
+def fp8_gemm_blockscaled_bf16a(a, b, sb, out_dtype="bf16", c=None, qa=None, sa=None,
+                               with_codes=False, stream=None):
+    """Quantize-on-load GEMM: a is bf16 M x K, quantized to 1x128 tiles inside
+    the GEMM. Returns c, or (c, qa, sa) with with_codes (A's codes and scales,
+    as fp8q_quant_act_1x128 gives them)."""
+    torch = _torch()
+    code, tdt = _out_dtype(out_dtype)
+    pa = _dev(a, "a", torch.bfloat16, 2)
+    pb = _dev(b, "b", torch.uint8, 2)
+    psb = _dev(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if K % 128 == 0 and N % 128 == 0 and tuple(sb.shape) != (N // 128, K // 128):
+        raise ValueError("sb must have shape (N/128, K/128)")
+    c = _out(c, "c", (M, N), tdt, a.device)
+    pq = ps = None
+    if with_codes or qa is not None or sa is not None:
+        qa = _out(qa, "qa", (M, K), torch.uint8, a.device)
+        sa = _out(sa, "sa", (M, K // 128), torch.float32, a.device)
+        pq, ps = qa.data_ptr(), sa.data_ptr()
+    _check("fp8_gemm_blockscaled_bf16a",
+           lib().fp8_gemm_blockscaled_bf16a(pa, pb, psb, c.data_ptr(), code, M, N, K, pq, ps,
+                                            _stream(stream)))
+    return (c, qa, sa) if pq is not None else c
 
 
 def fp8_gemm_blockscaled_ws(a, sa, b, sb, out_dtype="bf16", c=None, workspace=None, stream=None):

@@ -14,8 +14,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfp8q.so")
 
-SOURCES = ["quant.hip", "retile.hip", "norm.hip", "moe.hip", "gemm.hip", "api.cpp"]
-HEADERS = ["common.hpp"]
+SOURCES = ["quant.hip", "retile.hip", "norm.hip", "moe.hip", "gemm.hip", "gemm_qa.hip", "api.cpp"]
+HEADERS = ["common.hpp", "tiles.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

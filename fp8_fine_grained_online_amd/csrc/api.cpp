@@ -28,6 +28,9 @@ hipError_t launch_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const u
 hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b,
                                  const float* sb_rows, void* c, bool bf16_out, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream);
+hipError_t launch_gemm_quant_a(const void* a, const uint8_t* b, const float* sb, void* c,
+                               bool bf16_out, int64_t M, int64_t N, int64_t K, uint8_t* qa,
+                               float* sa, hipStream_t stream);
 hipError_t launch_quant_act_128x1(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
                                   hipStream_t stream);
 hipError_t launch_norm_quant_act_1x128(const void* x, const void* gamma, const void* beta,
@@ -117,7 +120,7 @@ int check_retile(const void* in, const float* in_s, bool need_in_s, int64_t R, i
 
 extern "C" {
 
-int fp8q_version(void) { return 200; }
+int fp8q_version(void) { return 201; }
 
 const char* fp8q_status_string(int status) {
   switch (status) {
@@ -163,6 +166,28 @@ int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b, co
   if ((s = check_device())) return s;
   return launched(fp8q::launch_gemm_blockscaled(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16, M, N,
                                                 K, (hipStream_t)stream));
+}
+
+int fp8_gemm_blockscaled_bf16a(const void* a, const uint8_t* b, const float* sb, void* c,
+                               int out_dtype, int64_t M, int64_t N, int64_t K, uint8_t* qa, float* sa,
+                               void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
+  if (N % kGroup || K % kGroup) return FP8Q_ERR_SHAPE;
+  if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_DTYPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxK) return FP8Q_ERR_TOO_LARGE;
+  if ((M + 127) / 128 * ((N + 255) / 256) > kMaxDim) return FP8Q_ERR_TOO_LARGE;
+  if (M == 0 || N == 0) return FP8Q_OK;  // valid no-op (no outputs written)
+  if (!c) return FP8Q_ERR_NULL;
+  if ((qa == nullptr) != (sa == nullptr)) return FP8Q_ERR_NULL;  // both outputs or neither
+  if (K > 0 && (!a || !b || !sb)) return FP8Q_ERR_NULL;         // K == 0 reads no operand
+  if (!aligned(c, 16)) return FP8Q_ERR_ALIGN;
+  if (K > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(sb, 4))) return FP8Q_ERR_ALIGN;
+  if (qa && (!aligned(qa, 16) || !aligned(sa, 4))) return FP8Q_ERR_ALIGN;
+  int s;
+  if ((s = check_device())) return s;
+  return launched(fp8q::launch_gemm_quant_a(a, b, sb, c, out_dtype == FP8Q_OUT_BF16, M, N, K,
+                                            K > 0 ? qa : nullptr, K > 0 ? sa : nullptr,
+                                            (hipStream_t)stream));
 }
 
 int64_t fp8_gemm_blockscaled_ws_bytes(int64_t M, int64_t N, int64_t K) {

@@ -87,11 +87,14 @@ class Workload:
     tokens: int = 0  # grouped: real tokens before padding
     backward: bool = False  # Dgrad + Wgrad of the layer Y[M x N] = X[M x K] W[N x K]^T
     topk: int = 0  # MoE dispatch: router choices per token (M = tokens)
+    quant_on_load: bool = False  # A quantized inside the GEMM (fp8_gemm_blockscaled_bf16a)
 
 
 WORKLOADS = {
     "dense_256x256x1024": Workload(0, "dense_256x256x1024", 256, 256, 1024, ["f32", "bf16"]),
     "dense_4096x4096x4096": Workload(1, "dense_4096x4096x4096", 4096, 4096, 4096),
+    # the same inputs (same id) through the quantize-on-load GEMM
+    "qol_4096x4096x4096": Workload(1, "qol_4096x4096x4096", 4096, 4096, 4096, quant_on_load=True),
     "proj_8192x7168x2048": Workload(20, "proj_8192x7168x2048", 8192, 7168, 2048),
     "proj_8192x2048x7168": Workload(21, "proj_8192x2048x7168", 8192, 2048, 7168),
     "bwd_proj_8192x7168x2048": Workload(22, "bwd_proj_8192x7168x2048", 8192, 7168, 2048,

@@ -153,6 +153,32 @@ FP8Q_API int fp8_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const ui
                                      int64_t K, void* workspace, int64_t workspace_bytes,
                                      void* stream);
 
+/*
+ * Quantize-on-load GEMM: C = Q(A) * B^T with A given in bf16, where Q is the
+ * 1x128 activation quantization of fp8q_quant_act_1x128, done inside the
+ * GEMM's load stage (each K group of A is read in bf16, quantized in
+ * registers and written to LDS as E4M3 codes + scale for the matrix cores).
+ * Results equal fp8q_quant_act_1x128 followed by fp8_gemm_blockscaled: the
+ * same codes and scales, the same per-group promotion (up to the FP32
+ * summation order of the MFMAs, within that call's tolerance).
+ * Source: the woojincopolymer.co.kr post, paragraph of hardware suggestions
+ * (fuse the FP8 cast with the global-to-shared transfer); the arithmetic of
+ * fp8q_quant_act_1x128 and fp8_gemm_blockscaled.
+ *
+ *   a_bf16 : in,  M x K bf16, row-major, 16-byte aligned
+ *   b, sb  : in,  as for fp8_gemm_blockscaled (N x K E4M3, (N/128) x (K/128))
+ *   c      : out, M x N (float32 or bfloat16 per out_dtype), 16-byte aligned
+ *   qa, sa : optional outputs (both NULL or both set): the codes (M x K,
+ *            16-byte aligned) and scales (M x (K/128)) of A, bit-identical to
+ *            fp8q_quant_act_1x128's; written when M, N and K are all > 0
+ * Requires N % 128 == 0 and K % 128 == 0; M arbitrary. M == 0 or N == 0 is a
+ * no-op; K == 0 writes zeros to c. Each of the N/256 column tiles quantizes
+ * its rows of A again (the price of the fusion on this hardware).
+ */
+FP8Q_API int fp8_gemm_blockscaled_bf16a(const void* a_bf16, const uint8_t* b, const float* sb,
+                                        void* c, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                        uint8_t* qa, float* sa, void* stream);
+
 /* Workspace bytes fp8_gemm_blockscaled_ws needs for this shape (0: none; -1: invalid). */
 FP8Q_API int64_t fp8_gemm_blockscaled_ws_bytes(int64_t M, int64_t N, int64_t K);
 

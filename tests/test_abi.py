@@ -27,7 +27,8 @@ def declared_symbols():
 ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
                 "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
                 "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1",
-                "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8_gemm_blockscaled_ws"]
+                "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8_gemm_blockscaled_ws",
+                "fp8_gemm_blockscaled_bf16a"]
 
 
 def test_header_declares_the_entry_points():
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib()
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert L.fp8q_version() == 200
+    assert L.fp8q_version() == 201
     for s in range(8):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"
@@ -238,6 +239,22 @@ def test_gemm_ws_validation():
     assert f(None, None, None, None, None, 0, 0, 128, 128, None, 0, None) == 0
 
 
+def test_quant_on_load_gemm_validation():
+    L = _lib()
+    f = L.fp8_gemm_blockscaled_bf16a
+    assert f(X, B, SB, C, 1, 64, 100, 128, None, None, None) == 2   # N % 128
+    assert f(X, B, SB, C, 1, 64, 128, 100, None, None, None) == 2   # K % 128
+    assert f(X, B, SB, C, 7, 64, 128, 128, None, None, None) == 4   # out dtype
+    assert f(X, B, SB, None, 1, 64, 128, 128, None, None, None) == 1
+    assert f(None, B, SB, C, 1, 64, 128, 128, None, None, None) == 1
+    assert f(X, B, SB, C, 1, 64, 128, 128, Q, None, None) == 1      # codes without scales
+    assert f(X + 8, B, SB, C, 1, 64, 128, 128, None, None, None) == 3
+    assert f(X, B, SB, C, 1, 64, 128, 128, Q + 8, SA, None) == 3
+    assert f(X, B, SB, C, 1, 64, 128, (1 << 23) + 128, None, None, None) == 7
+    assert f(None, None, None, None, 1, 0, 128, 128, None, None, None) == 0
+    assert f(None, None, None, C, 1, 64, 128, 0, None, None, None) in (0, 6)  # K == 0: no operands
+
+
 def test_rowscaled_gemm_validation():
     L = _lib()
     f = L.fp8_gemm_rowscaled
@@ -258,6 +275,7 @@ def test_valid_call_without_gpu_reports_no_device():
     L = _lib()
     assert L.fp8q_quant_act_1x128(X, 4, 128, Q, SA, None) == 6
     assert L.fp8_gemm_blockscaled(A, SA, B, SB, C, 1, 64, 128, 128, None) == 6
+    assert L.fp8_gemm_blockscaled_bf16a(X, B, SB, C, 1, 64, 128, 128, Q, SA, None) == 6
     assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
     assert L.fp8q_quant_act_1x128_128x1(X, 128, 128, Q, SA, B, SB, None) == 6
     assert L.fp8q_norm_quant_act_1x128(X, B, None, 1e-6, 0, 4, 128, Q, SA, None) == 6
