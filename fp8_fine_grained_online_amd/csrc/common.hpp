@@ -48,6 +48,30 @@ __device__ __forceinline__ uint32_t row8_max_u32(uint32_t v) {
   return v;
 }
 
+// Tile scale s = fl32(amax / 448), the correctly rounded binary32 quotient.
+// For amax >= 2^-116 (every quotient normal) it is one multiply by
+// c = RN(1/448) and one FMA correction, q0 = RN(amax c), then
+// q = RN(q0 + RN(amax - 448 q0) c): an exhaustive host comparison over every
+// binary32 amax found it equal to the correctly rounded quotient wherever
+// that quotient is normal, and only there, so smaller amax take the IEEE
+// division (a branch no tile of ordinary data takes).
+__device__ __forceinline__ float tile_scale(float amax) {
+  constexpr float kInv448 = 1.0f / 448.0f;  // RN(1/448)
+  if (amax < 0x1p-116f) return __fdiv_rn(amax, kFp8Max);
+  const float q0 = amax * kInv448;
+  return __builtin_fmaf(__builtin_fmaf(-q0, kFp8Max, amax), kInv448, q0);
+}
+
+// RN(1/x) for binary32 x in [2^-85, 2^120): one Newton step from the hardware
+// reciprocal estimate, r = RN(r0 + RN(1 - x r0) r0) with r0 = v_rcp_f32(x).
+// An exhaustive GPU comparison with the IEEE division over every binary32 in
+// that range found no difference (outside it, for subnormal x or a subnormal
+// result, there are).
+__device__ __forceinline__ float recip_rn(float x) {
+  const float r0 = __builtin_amdgcn_rcpf(x);
+  return __builtin_fmaf(__builtin_fmaf(-x, r0, 1.0f), r0, r0);
+}
+
 // Per-tile quotient x / s, correctly rounded in binary32.
 //
 // The divide is replaced by a reciprocal and one FMA correction
@@ -78,7 +102,9 @@ __device__ __forceinline__ TileDivisor make_divisor(float s, float amax) {
   }
   d.p = (amax < 0x1p-64f) ? 0x1p+64f : 1.0f;
   d.sp = s * d.p;  // exact: power-of-two scaling of a finite value
-  d.r = __fdiv_rn(1.0f, d.sp);
+  // s > 0 here, so s >= 2^-149 and sp >= 2^-85 (tiny tiles are scaled by
+  // 2^64); sp <= FLT_MAX / 448 < 2^120: inside recip_rn's verified range
+  d.r = recip_rn(d.sp);
   return d;
 }
 

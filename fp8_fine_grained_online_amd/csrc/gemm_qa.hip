@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kQaThreads) void gemm_qa_kernel(QaArgs p) {
     for (int i = 0; i < kQaChunks; ++i) {
       const int row = qrow0 + 32 * i;
       const float amax = __uint_as_float(row16_max_u32(__float_as_uint(absmax8(r[i]))));
-      const float s = __fdiv_rn(amax, kFp8Max);
+      const float s = tile_scale(amax);
       const TileDivisor d = make_divisor(s, amax);
       const uint2 codes = quant8(r[i], d);
       *(uint2*)(stage + swz(row, qc >> 1) + (qc & 1) * 8) = codes;

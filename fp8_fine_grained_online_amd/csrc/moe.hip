@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void dispatch_quant_kernel(const uint4* __rest
       const bool have = c < n_chunks;
       const float m = fmaxf(absmax8(v[u][0]), absmax8(v[u][1]));
       const float amax = __uint_as_float(row8_max_u32(__float_as_uint(m)));
-      const float s = __fdiv_rn(amax, kFp8Max);
+      const float s = tile_scale(amax);
       const TileDivisor d = make_divisor(s, amax);
       const uint2 lo = quant8(v[u][0], d), hi = quant8(v[u][1], d);
       const uint4 codes = make_uint4(lo.x, lo.y, hi.x, hi.y);

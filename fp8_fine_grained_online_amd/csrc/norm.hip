@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_quant_1x128_kernel(
       m = fmaxf(m, fabsf(y[e]));
     }
     const float amax = __uint_as_float(row16_max_u32(__float_as_uint(m)));
-    const float s = __fdiv_rn(amax, kFp8Max);
+    const float s = tile_scale(amax);
     const TileDivisor d = make_divisor(s, amax);
     uint2 out;
     out.x = pack4_e4m3(quotient(y[0], d), quotient(y[1], d), quotient(y[2], d), quotient(y[3], d));

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kActThreads) void quant_act_1x128_kernel(
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
     // non-negative floats order like their bit patterns
     const float amax = __uint_as_float(row16_max_u32(__float_as_uint(m)));
-    const float s = __fdiv_rn(amax, kFp8Max);
+    const float s = tile_scale(amax);
     const TileDivisor d = make_divisor(s, amax);
     uint2 out;
     out.x = pack4_e4m3(quotient(f[0], d), quotient(f[1], d), quotient(f[2], d), quotient(f[3], d));
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
   __syncthreads();
   mb = umax(umax(wave_max[0], wave_max[1]), umax(wave_max[2], wave_max[3]));
   const float amax = __uint_as_float(mb);
-  const float s = __fdiv_rn(amax, kFp8Max);
+  const float s = tile_scale(amax);
   const TileDivisor d = make_divisor(s, amax);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kRtThreads) void retile_kernel(const uint8_t* __res
     const uint32_t mb = __float_as_uint(m);
     const float amax = __uint_as_float(
         umax(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, false)));
-    const float s = __fdiv_rn(amax, kFp8Max);
+    const float s = tile_scale(amax);
     const TileDivisor d = make_divisor(s, amax);
     uint8_t* dst = row_q + ((int64_t)rt * 128 + row) * C + (int64_t)ct * 128 + half * 64;
 #pragma unroll
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kRtThreads) void retile_kernel(const uint8_t* __res
     if (h == 0) full_max[k] = fmaxf(m, half_max[k]);
     __syncthreads();
     const float amax = full_max[k];
-    const float s = __fdiv_rn(amax, kFp8Max);
+    const float s = tile_scale(amax);
     const TileDivisor d = make_divisor(s, amax);
 #pragma unroll
     for (int j = 0; j < 16; ++j)
