@@ -25,7 +25,7 @@ namespace fp8q {
 // kActUnroll chunks spaced one block-width apart, all loads issued first.
 // ---------------------------------------------------------------------------
 constexpr int kActThreads = 256;
-constexpr int kActUnroll = 4;
+constexpr int kActUnroll = 2;
 
 __global__ __launch_bounds__(kActThreads) void quant_act_1x128_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ sa, int64_t n_tiles) {
