@@ -24,7 +24,7 @@ def declared_symbols():
     return re.findall(r"FP8Q_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
 
 
-ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
+ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_act_1x128_nt", "fp8q_quant_weight_128x128", "fp8_gemm_blockscaled",
                 "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
                 "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1",
                 "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8_gemm_blockscaled_ws",
@@ -41,20 +41,23 @@ def test_library_exports_every_declared_symbol():
     L = _lib()
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert L.fp8q_version() == 201
+    assert L.fp8q_version() == 202
     for s in range(8):
         assert L.fp8q_status_string(s)
     assert L.fp8q_status_string(99) == b"unknown status"
 
 
-# fake, suitably aligned addresses: never dereferenced, validation fails first
+# Fake, suitably aligned addresses. They must never reach a kernel: every call
+# that uses them either fails validation or is a no-op before any HIP call, or
+# runs only without a GPU (where it stops at the device check, status 6).
 P = 0x100000
 A, SA, B, SB, C, OFF, X, Q = (P * i for i in range(1, 9))
 
 
-def test_quant_act_validation():
+@pytest.mark.parametrize("name", ["fp8q_quant_act_1x128", "fp8q_quant_act_1x128_nt"])
+def test_quant_act_validation(name):
     L = _lib()
-    f = L.fp8q_quant_act_1x128
+    f = getattr(L, name)
     assert f(X, 4, 100, Q, SA, None) == 2  # K % 128
     assert f(X, -1, 128, Q, SA, None) == 2
     assert f(X, 4, -128, Q, SA, None) == 2
@@ -219,9 +222,13 @@ def test_dispatch_sizes_and_validation():
         assert call(**{name: None}) == 1, name
     assert call(x=X + 8) == 3 and call(q=Q + 4) == 3 and call(ids=SB + 2) == 3
     assert call(sa=SA + 2) == 3 and call(off=OFFS + 2) == 3 and call(ws=WS + 2) == 3
-    # T = 0 needs no token pointers but still writes m_offsets
-    assert call(T=0, x=None, ids=None, rows=None, cap=L.fp8q_moe_dispatch_max_rows(0, 2, 4),
-                wsb=L.fp8q_moe_dispatch_workspace_bytes(0, 2, 4)) in (0, 6)
+    # T = 0 needs no token pointers. It passes validation and then writes
+    # m_offsets, so with a GPU present it would write through the fake OFFS:
+    # only without a device (status 6). With real buffers it is covered by
+    # test_gpu_moe.py::test_no_tokens_writes_zero_offsets.
+    if not gpu_available():
+        assert call(T=0, x=None, ids=None, rows=None, cap=L.fp8q_moe_dispatch_max_rows(0, 2, 4),
+                    wsb=L.fp8q_moe_dispatch_workspace_bytes(0, 2, 4)) == 6
 
 
 def test_gemm_ws_validation():
@@ -252,7 +259,11 @@ def test_quant_on_load_gemm_validation():
     assert f(X, B, SB, C, 1, 64, 128, 128, Q + 8, SA, None) == 3
     assert f(X, B, SB, C, 1, 64, 128, (1 << 23) + 128, None, None, None) == 7
     assert f(None, None, None, None, 1, 0, 128, 128, None, None, None) == 0
-    assert f(None, None, None, C, 1, 64, 128, 0, None, None, None) in (0, 6)  # K == 0: no operands
+    # K == 0 reads no operand but zero-fills C: with a GPU present it would
+    # write through the fake C, so only without a device (status 6). With a real
+    # C it is covered by test_gpu_gemm_qa.py::test_k_zero_writes_zeros_and_m_zero_is_a_no_op.
+    if not gpu_available():
+        assert f(None, None, None, C, 1, 64, 128, 0, None, None, None) == 6
 
 
 def test_rowscaled_gemm_validation():
@@ -274,6 +285,7 @@ def test_rowscaled_gemm_validation():
 def test_valid_call_without_gpu_reports_no_device():
     L = _lib()
     assert L.fp8q_quant_act_1x128(X, 4, 128, Q, SA, None) == 6
+    assert L.fp8q_quant_act_1x128_nt(X, 4, 128, Q, SA, None) == 6
     assert L.fp8_gemm_blockscaled(A, SA, B, SB, C, 1, 64, 128, 128, None) == 6
     assert L.fp8_gemm_blockscaled_bf16a(X, B, SB, C, 1, 64, 128, 128, Q, SA, None) == 6
     assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
