@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20     # MI355X Infinity Cache
 # sources whose hash keys the recorded counters of each streaming kernel
 STREAM_SOURCES = {"quant_act_1x128": ("quant.hip", "common.hpp"),
+                  "quant_act_1x128_nt": ("quant.hip", "common.hpp"),
                   "norm_quant_act_1x128": ("norm.hip", "common.hpp"),
                   "moe_dispatch_1x128": ("moe.hip", "common.hpp")}
 
@@ -125,8 +126,10 @@ def cpu_baseline_grouped(workload, a_bits, b_bits, off, counts, budget_s=10.0):
     }
 
 
-def copy_calibration(steps, warmup):
-    """A plain 512 MiB device-to-device copy: bytes moved are known exactly."""
+def copy_rate(steps, warmup):
+    """A plain 512 MiB device-to-device copy (bytes moved known exactly; the
+    source is twice the Infinity Cache, so it streams from HBM). Returns
+    (bytes each way, ms per copy)."""
     import torch
     n = 512 << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
@@ -142,9 +145,30 @@ def copy_calibration(steps, warmup):
         dst.copy_(src)
     t1.record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    return n, t0.elapsed_time(t1) / steps
+
+
+def copy_calibration(steps, warmup):
+    n, ms = copy_rate(steps, warmup)
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 5),
                       "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def read_sclk():
+    """The GPU's current shader-clock level as the driver reports it
+    (pp_dpm_sclk of the device's PCI node), or None where it is not readable."""
+    import torch
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        node = "/sys/bus/pci/devices/%04x:%02x:%02x.0/pp_dpm_sclk" % (
+            pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
+        with open(node) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].strip().rstrip("*").strip()
+    except (AttributeError, OSError, ValueError, IndexError, RuntimeError):
+        pass
+    return None
 
 
 def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
@@ -310,8 +334,10 @@ def plan_stream(w, args, F, S, L, dev, sp, up_bf16):
         nbytes += 2 * K
         cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, M, g_bits)
     else:
-        name = "quant_act_1x128"
-        fn = lambda: L.fp8q_quant_act_1x128(X.data_ptr(), M, K, q.data_ptr(), sa.data_ptr(), sp)
+        # standalone quantization: nothing reads the codes next on this GPU, so
+        # the non-temporal-store form (same codes, not kept in the cache)
+        name = "quant_act_1x128_nt"
+        fn = lambda: L.fp8q_quant_act_1x128_nt(X.data_ptr(), M, K, q.data_ptr(), sa.data_ptr(), sp)
         cpu = lambda: cpu_baseline_stream(args.workload, x_bits, nbytes / M, M, None)
     return {
         "launches": [(name, fn)],
@@ -542,10 +568,17 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
+    sclk = []  # the driver's clock level, read on the host while steps run
     for i in range(args.steps):
         step(evs[i])
+        sclk.append(read_sclk())
     torch.cuda.synchronize()
-    kms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    mhz = [int(v.lower().replace("mhz", "")) for v in sclk if v and v.lower().endswith("mhz")
+           and v[:-3].isdigit()]
+    per_launch = {n: np.array([e[i].elapsed_time(e[i + 1]) for e in evs]) for i, n in enumerate(names)}
+    kms = {n: float(v.mean()) for n, v in per_launch.items()}
+    kpct = {n: [round(float(x), 5) for x in np.percentile(v, [10, 50, 90])]
+            for n, v in per_launch.items()}
     if len(names) == 1:
         # one launch per step: the step timing (events only at the ends of the
         # timed pass) is that kernel's duration without per-launch marker cost
@@ -600,6 +633,9 @@ def main():
                        buffer_MB_per_copy=round(resident / 1e6, 1)),
         "roofline": roofline,
         "kernels_ms": {n: round(v, 5) for n, v in kms.items()},
+        "kernels_ms_p10_p50_p90": kpct,
+        "sclk_driver_mhz": ({"median": int(np.median(mhz)), "max": max(mhz), "samples": len(mhz)}
+                            if mhz else None),
         "kernels_GBps": {n: round(b / (kms[n] * 1e-3) / 1e9, 1) for n, b in plan["bytes"].items()},
         "kernels_TFLOPs": {n: round(f / (kms[n] * 1e-3) / 1e12, 2) for n, f in plan["flops"].items()},
         "wall_s_timed": round(wall, 4),
@@ -607,6 +643,12 @@ def main():
     }
     for key, (n, f) in plan["extra"].items():
         out[key] = round(f / (kms[n] * 1e-3) / 1e12, 2)
+    if roofline["bound"] == "hbm":
+        # practical ceiling: a plain device-to-device copy on this GPU
+        n_copy, ms_copy = copy_rate(20, 5)
+        copy_gbps = 2 * n_copy / (ms_copy * 1e-3) / 1e9
+        roofline["copy_GBps"] = round(copy_gbps, 1)
+        roofline["frac_of_copy"] = round(roofline["achieved"] / copy_gbps, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = plan["cpu"]()
     print(json.dumps(out), flush=True)

@@ -9,6 +9,7 @@ if the library is missing, every call raises.
 
 Entry points (same names as the C ABI):
   fp8q_quant_act_1x128(x)                    -> (q, sa)
+  fp8q_quant_act_1x128_nt(x)                 -> (q, sa)   same, non-temporal stores
   fp8q_quant_weight_128x128(w)               -> (q, sb)
   fp8_gemm_blockscaled(a, sa, b, sb, out_dtype)          -> c
   fp8_gemm_blockscaled_ws(a, sa, b, sb, out_dtype)       -> c   (split-K for small M)
@@ -39,6 +40,7 @@ from ._lib import (  # noqa: F401
     fp8q_norm_quant_act_1x128,
     fp8q_moe_dispatch_1x128,
     fp8q_quant_act_1x128,
+    fp8q_quant_act_1x128_nt,
     fp8q_requant_1x128_to_128x1,
     fp8q_transpose_weight_128x128,
     fp8q_quant_weight_128x128,
@@ -49,7 +51,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "Fp8qError", "FP8Q_OUT_BF16", "FP8Q_OUT_F32", "STATUS",
-    "fp8q_quant_act_1x128", "fp8q_quant_weight_128x128",
+    "fp8q_quant_act_1x128", "fp8q_quant_act_1x128_nt", "fp8q_quant_weight_128x128",
     "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_bf16a", "fp8_gemm_blockscaled_ws", "fp8_gemm_grouped", "fp8q_version", "lib", "lib_path",
     "fp8q_quant_act_128x1", "fp8q_quant_act_1x128_128x1", "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8q_requant_1x128_to_128x1", "fp8q_transpose_weight_128x128",
     "fp8_gemm_rowscaled",

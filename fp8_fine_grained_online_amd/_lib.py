@@ -43,6 +43,8 @@ def lib() -> ctypes.CDLL:
         L.fp8q_status_string.argtypes = [i32]
         L.fp8q_quant_act_1x128.restype = i32
         L.fp8q_quant_act_1x128.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.fp8q_quant_act_1x128_nt.restype = i32
+        L.fp8q_quant_act_1x128_nt.argtypes = [vp, i64, i64, vp, vp, vp]
         L.fp8q_quant_weight_128x128.restype = i32
         L.fp8q_quant_weight_128x128.argtypes = [vp, i64, i64, vp, vp, vp]
         L.fp8_gemm_blockscaled.restype = i32
@@ -133,6 +135,19 @@ def fp8q_quant_act_1x128(x, q=None, sa=None, stream=None):
     sa = _out(sa, "sa", (M, K // 128 if K % 128 == 0 else 0), torch.float32, x.device)
     _check("fp8q_quant_act_1x128",
            lib().fp8q_quant_act_1x128(px, M, K, q.data_ptr(), sa.data_ptr(), _stream(stream)))
+    return q, sa
+
+
+def fp8q_quant_act_1x128_nt(x, q=None, sa=None, stream=None):
+    """fp8q_quant_act_1x128 with non-temporal stores (same results; for codes
+    that are not read next on this GPU)."""
+    torch = _torch()
+    px = _dev(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    q = _out(q, "q", (M, K), torch.uint8, x.device)
+    sa = _out(sa, "sa", (M, K // 128 if K % 128 == 0 else 0), torch.float32, x.device)
+    _check("fp8q_quant_act_1x128_nt",
+           lib().fp8q_quant_act_1x128_nt(px, M, K, q.data_ptr(), sa.data_ptr(), _stream(stream)))
     return q, sa
 
 

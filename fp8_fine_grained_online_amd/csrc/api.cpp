@@ -11,7 +11,7 @@
 
 namespace fp8q {
 hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
-                                  hipStream_t stream);
+                                  bool nontemporal, hipStream_t stream);
 hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* q, float* sb,
                                        hipStream_t stream);
 hipError_t launch_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
@@ -120,7 +120,7 @@ int check_retile(const void* in, const float* in_s, bool need_in_s, int64_t R, i
 
 extern "C" {
 
-int fp8q_version(void) { return 201; }
+int fp8q_version(void) { return 202; }
 
 const char* fp8q_status_string(int status) {
   switch (status) {
@@ -136,15 +136,25 @@ const char* fp8q_status_string(int status) {
   }
 }
 
-int fp8q_quant_act_1x128(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,
-                         void* stream) {
+static int quant_act_1x128(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,
+                           bool nontemporal, void* stream) {
   if (M < 0 || K < 0 || K % kGroup) return FP8Q_ERR_SHAPE;
   if (M > kMaxDim || K > kMaxDim || M * (K / kGroup) > (kMaxDim / 16)) return FP8Q_ERR_TOO_LARGE;
   if (M == 0 || K == 0) return FP8Q_OK;
   if (!x_bf16 || !q || !sa) return FP8Q_ERR_NULL;
   if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(sa, 4)) return FP8Q_ERR_ALIGN;
   if (int s = check_device()) return s;
-  return launched(fp8q::launch_quant_act_1x128(x_bf16, M, K, q, sa, (hipStream_t)stream));
+  return launched(fp8q::launch_quant_act_1x128(x_bf16, M, K, q, sa, nontemporal, (hipStream_t)stream));
+}
+
+int fp8q_quant_act_1x128(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,
+                         void* stream) {
+  return quant_act_1x128(x_bf16, M, K, q, sa, false, stream);
+}
+
+int fp8q_quant_act_1x128_nt(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,
+                            void* stream) {
+  return quant_act_1x128(x_bf16, M, K, q, sa, true, stream);
 }
 
 int fp8q_quant_weight_128x128(const void* w_bf16, int64_t N, int64_t K, uint8_t* q, float* sb,

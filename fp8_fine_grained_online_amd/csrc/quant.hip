@@ -10,7 +10,8 @@
 // Both kernels are HBM-streaming: 2 bytes read, 1 byte + 4/128 bytes written
 // per element. Loads and stores are 16-byte / 8-byte per lane and coalesced.
 // The bf16 inputs are read once (non-temporal loads); the codes and scales are
-// stored normally so that the GEMM consuming them next finds them in cache.
+// stored normally so that the GEMM consuming them next finds them in cache
+// (the activation kernel also has a non-temporal-store form).
 #include "common.hpp"
 
 namespace fp8q {
@@ -23,10 +24,13 @@ namespace fp8q {
 // 16 chunks of 16 bytes (8 bf16), one chunk per lane, so a DPP row of 16 lanes
 // owns one tile and reduces its amax with four DPP steps. Each thread handles
 // kActUnroll chunks spaced one block-width apart, all loads issued first.
+// kNt: codes and scales go out with non-temporal stores, which do not keep
+// them in the Infinity Cache (for outputs that are not read next on this GPU).
 // ---------------------------------------------------------------------------
 constexpr int kActThreads = 256;
 constexpr int kActUnroll = 2;
 
+template <bool kNt>
 __global__ __launch_bounds__(kActThreads) void quant_act_1x128_kernel(
     const uint4* __restrict__ x, uint2* __restrict__ q, float* __restrict__ sa, int64_t n_tiles) {
   const int64_t n_chunks = n_tiles * 16;
@@ -53,8 +57,14 @@ __global__ __launch_bounds__(kActThreads) void quant_act_1x128_kernel(
     out.x = pack4_e4m3(quotient(f[0], d), quotient(f[1], d), quotient(f[2], d), quotient(f[3], d));
     out.y = pack4_e4m3(quotient(f[4], d), quotient(f[5], d), quotient(f[6], d), quotient(f[7], d));
     if (c < n_chunks) {
-      q[c] = out;  // ordinary store: the GEMM reads the codes next, keep them cached
-      if ((threadIdx.x & 15) == 0) sa[c >> 4] = s;
+      if constexpr (kNt) {
+        __builtin_nontemporal_store(out.x, &q[c].x);
+        __builtin_nontemporal_store(out.y, &q[c].y);
+        if ((threadIdx.x & 15) == 0) __builtin_nontemporal_store(s, &sa[c >> 4]);
+      } else {
+        q[c] = out;  // ordinary store: a GEMM reading the codes next finds them cached
+        if ((threadIdx.x & 15) == 0) sa[c >> 4] = s;
+      }
     }
   }
 }
@@ -104,12 +114,16 @@ __global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
 }
 
 hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
-                                  hipStream_t stream) {
+                                  bool nontemporal, hipStream_t stream) {
   const int64_t n_tiles = M * (K / kGroup);
   const int64_t per_block = (int64_t)kActThreads * kActUnroll / 16;  // tiles per block
   const int64_t blocks = (n_tiles + per_block - 1) / per_block;
-  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(kActThreads), 0, stream,
-                     (const uint4*)x, (uint2*)q, sa, n_tiles);
+  if (nontemporal)
+    hipLaunchKernelGGL(quant_act_1x128_kernel<true>, dim3((unsigned)blocks), dim3(kActThreads), 0,
+                       stream, (const uint4*)x, (uint2*)q, sa, n_tiles);
+  else
+    hipLaunchKernelGGL(quant_act_1x128_kernel<false>, dim3((unsigned)blocks), dim3(kActThreads), 0,
+                       stream, (const uint4*)x, (uint2*)q, sa, n_tiles);
   return hipGetLastError();
 }
 

@@ -17,10 +17,11 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
-def gpu_act(bits):
+def gpu_act(bits, nt=False):
     import fp8_fine_grained_online_amd as F
     import torch
-    q, sa = F.fp8q_quant_act_1x128(to_dev_bf16(bits))
+    f = F.fp8q_quant_act_1x128_nt if nt else F.fp8q_quant_act_1x128
+    q, sa = f(to_dev_bf16(bits))
     torch.cuda.synchronize()
     return q.cpu().numpy(), sa.cpu().numpy()
 
@@ -49,6 +50,7 @@ def test_exhaustive_table(exp_field):
     tiles = S.exhaustive_tiles(exp_field)
     want = quant.quant_act_1x128(tiles)
     assert_same(*gpu_act(tiles), *want)
+    assert_same(*gpu_act(tiles, nt=True), *want)  # the non-temporal-store form
     # the same rows through the weight kernel, 128 rows per block
     rows = tiles.shape[0] // 128 * 128
     w = tiles[:rows]
@@ -56,10 +58,11 @@ def test_exhaustive_table(exp_field):
 
 
 @pytest.mark.parametrize("M,K", [(1, 128), (3, 384), (257, 1024), (64, 7168), (1000, 256)])
-def test_random_shapes(M, K):
+@pytest.mark.parametrize("nt", [False, True])
+def test_random_shapes(M, K, nt):
     from oracle import quant
     x = S.activations(M, K, S.rng_for(500 + M, K))
-    assert_same(*gpu_act(x), *quant.quant_act_1x128(x))
+    assert_same(*gpu_act(x, nt), *quant.quant_act_1x128(x))
 
 
 @pytest.mark.parametrize("N,K", [(128, 128), (384, 256), (256, 7168)])
@@ -112,6 +115,11 @@ def test_full_size_activation_sampled_rows_and_determinism():
     rows = np.unique(np.concatenate([[0, 1, w.M - 1], S.rng_for(720, 0).integers(0, w.M, 61)]))
     want_q, want_s = quant.quant_act_1x128(x[rows])
     assert_same(q1.cpu().numpy()[rows], s1.cpu().numpy()[rows], want_q, want_s)
+    # the non-temporal-store form (the one the standalone workload times): every
+    # code and scale equal to the cached form's
+    q3, s3 = F.fp8q_quant_act_1x128_nt(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(q3, q1) and torch.equal(s3.view(torch.int32), s1.view(torch.int32))
 
 
 def test_full_size_weights_sampled_blocks():
