@@ -235,6 +235,17 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
             return cpu_baseline_grouped(args.workload, a_bits, b_bits, off, counts)
         return cpu_baseline(args.workload, a_bits, b_bits, M)  # the whole workload
 
+    def gemm_f32_corner(n):
+        """C[:n, :n] of this GEMM with FP32 output, from the operands the timed
+        steps quantized on the device."""
+        c32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+        st = L.fp8_gemm_blockscaled(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(),
+                                    c32.data_ptr(), F.FP8Q_OUT_F32, M, N, K, sp)
+        torch.cuda.synchronize()
+        if st:
+            raise RuntimeError(f"fp8_gemm_blockscaled failed with status {st}")
+        return c32[:n, :n].cpu().numpy()
+
     # algorithmic bytes of the GEMM: operands, scales and output, each once
     gemm_bytes = (M * K + b_rows * K + M * (K // 128) * 4 + (b_rows // 128) * (K // 128) * 4
                   + 2 * M * N)
@@ -254,7 +265,33 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
                    "step": " + ".join(name for name, _ in launches)},
         "extra": {"gemm_tflops_padded": (gemm_name, 2.0 * M * N * K)},
         "cpu": cpu,
+        # the limited-accumulation demonstration belongs to the K = 4096 GEMM
+        "accum": (lambda: accumulation_demo(a_bits, b_bits, gemm_f32_corner))
+                 if gemm_name == "fp8_gemm_blockscaled" and M >= 256 and N >= 256 and K == 4096
+                 else None,
     }
+
+
+def accumulation_demo(a_bits, b_bits, gpu_corner, n=256):
+    """The pages' limited-accumulation experiment (an FP8 GEMM with K = 4096
+    whose Tensor-Core accumulation loses nearly 2%), on C[:n, :n] of this
+    workload: the oracle's chunked 14-bit accumulator model and its per-group
+    FP32 promotion model, beside the GPU kernel's own FP32 output, each as the
+    largest relative error against the exact sum over outputs with
+    |C| >= 0.1 RMS(C). Quantizing only the sampled rows of A and of B is exact:
+    1x128 tiles and 128x128 blocks do not reach across rows or blocks."""
+    import numpy as np
+    from oracle import accsim, quant
+    t0 = time.perf_counter()
+    qa, sa = quant.quant_act_1x128(a_bits[:n])
+    qb, sb = quant.quant_weight_128x128(b_bits[:-(-n // 128) * 128])  # whole weight blocks
+    sb_rows = np.repeat(sb, 128, axis=0)[:n]
+    lim, pg, ref = accsim.demonstration(qa, sa, qb[:n], sb_rows, mant_bits=14, chunk=32, mode="rne")
+    gpu = accsim.max_rel_error(gpu_corner(n), ref)
+    return {"sample": f"C[0:{n}, 0:{n}], K = {qa.shape[1]}",
+            "metric": "max |C - C_exact| / |C_exact| over |C_exact| >= 0.1 RMS",
+            "limited_14bit_chunk32": round(lim, 5), "per_group_fp32_model": float(f"{pg:.3g}"),
+            "gpu_kernel_fp32_out": float(f"{gpu:.3g}"), "seconds": round(time.perf_counter() - t0, 1)}
 
 
 def plan_backward(w, args, F, S, L, dev, sp, up_bf16):
@@ -651,6 +688,8 @@ def main():
         roofline["frac_of_copy"] = round(roofline["achieved"] / copy_gbps, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = plan["cpu"]()
+        if plan.get("accum"):
+            out["accumulation_demo"] = plan["accum"]()
     print(json.dumps(out), flush=True)
 
 

@@ -74,3 +74,25 @@ def test_sclk_reader_never_raises():
     import bench
     v = bench.read_sclk()
     assert v is None or isinstance(v, str)
+
+
+def test_accumulation_demo_leg():
+    """The limited-accumulation leg on a 64 x 64 corner, with the oracle's own
+    FP32-rounded GEMM standing in for the GPU's output: the 14-bit model lands
+    near the pages' ~2%, and an FP32 result stays orders of magnitude below it."""
+    import bench
+    from fp8_fine_grained_online_amd import synthetic as S
+    from oracle import gemm, quant
+    a = S.activations(64, 4096, S.rng_for(991, 0))
+    b = S.weights(128, 4096, S.rng_for(991, 1))
+
+    def corner(n):
+        qa, sa = quant.quant_act_1x128(a[:n])
+        qb, sb = quant.quant_weight_128x128(b)
+        return gemm.gemm_blockscaled(qa, sa, qb, sb, "f32")[:n, :n]
+
+    d = bench.accumulation_demo(a, b, corner, n=64)
+    assert d["sample"] == "C[0:64, 0:64], K = 4096"
+    assert 0.005 <= d["limited_14bit_chunk32"] <= 0.08
+    assert d["gpu_kernel_fp32_out"] * 1000 <= d["limited_14bit_chunk32"]
+    assert d["per_group_fp32_model"] * 1000 <= d["limited_14bit_chunk32"]
