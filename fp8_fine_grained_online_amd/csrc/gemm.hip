@@ -228,8 +228,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   // The copies of the next group are spread over the MFMAs (one every
   // kCopyEvery MFMAs, pinned by scheduling-group hints): a wave issues in
   // order, and a burst of direct-to-LDS copies would hold back its MFMAs
-  // while the memory pipeline accepts them.
-  constexpr int kCopyEvery = (SUBM * SUBN) / kCopies > 0 ? (SUBM * SUBN) / kCopies : 1;
+  // while the memory pipeline accepts them. They start only after the step's
+  // first kCopyOff MFMAs: until then every wave's B-fragment reads are being
+  // served, and a copy's LDS write would compete with them for LDS bandwidth.
+  // Measured on MI355X at three shapes, one copy every 2 MFMAs from MFMA 3
+  // beats one every 3 from MFMA 0 by 1-4%.
+  constexpr int kCopyOff = 3;
+  constexpr int kCopyEvery = 2;
+  static_assert(kCopyOff + (kCopies - 1) * kCopyEvery < SUBM * SUBN, "the copies fit in a step");
   // acc += part * scale: one scale for the lane's four columns (128x128 B
   // blocks: sc1 = sa * sb), or one per column (kRowB: sa * sb_row, formed
   // here so that no per-column products stay live across MFMAs)
@@ -263,7 +269,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
 #pragma unroll
     for (int t = 0; t < SUBM * SUBN; ++t) {
       const int i = t / SUBN, j = t % SUBN;
-      if (t % kCopyEvery == 0 && t / kCopyEvery < kCopies) issue_copy(t / kCopyEvery, g_next, nxt);
+      if (t >= kCopyOff && (t - kCopyOff) % kCopyEvery == 0 && (t - kCopyOff) / kCopyEvery < kCopies)
+        issue_copy((t - kCopyOff) / kCopyEvery, g_next, nxt);
       if (j == 0) {
         sc = sav * sbv;
         if (i + 1 < SUBM) {
@@ -286,7 +293,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
       }
     }
     promote(acc[SUBM - 1][SUBN - 1], part_prev, sc_prev, sav, sbq[kRowB ? SUBN - 1 : 0]);
-    // scheduling hint: one copy, then kCopyEvery MFMAs, repeated
+    // scheduling hint: kCopyOff MFMAs, then one copy and kCopyEvery MFMAs, repeated
+    __builtin_amdgcn_sched_group_barrier(0x008, kCopyOff, 0);  // MFMA
 #pragma unroll
     for (int q = 0; q < kCopies; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // VMEM read (the copy)
