@@ -10,8 +10,9 @@
 // Both kernels are HBM-streaming: 2 bytes read, 1 byte + 4/128 bytes written
 // per element. Loads and stores are 16-byte / 8-byte per lane and coalesced.
 // The bf16 inputs are read once (non-temporal loads); the codes and scales are
-// stored normally so that the GEMM consuming them next finds them in cache
-// (the activation kernel also has a non-temporal-store form).
+// stored normally so that the GEMM consuming them next finds them in cache,
+// unless the codes are larger than that cache (then non-temporally, and the
+// activation kernel also has an explicitly non-temporal entry point).
 #include "common.hpp"
 
 namespace fp8q {
@@ -76,6 +77,7 @@ __global__ __launch_bounds__(kActThreads) void quant_act_1x128_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kWThreads = 256;
 
+template <bool kNt>
 __global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
     const uint4* __restrict__ w, uint2* __restrict__ q, float* __restrict__ sb, int64_t K,
     int nblk_k) {
@@ -108,17 +110,28 @@ __global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
   const TileDivisor d = make_divisor(s, amax);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    q[c0 + (int64_t)i * 16 * chunks_per_row] = quant8(v[i], d);
+    const uint2 o = quant8(v[i], d);
+    if constexpr (kNt) {
+      __builtin_nontemporal_store(o.x, &q[c0 + (int64_t)i * 16 * chunks_per_row].x);
+      __builtin_nontemporal_store(o.y, &q[c0 + (int64_t)i * 16 * chunks_per_row].y);
+    } else {
+      q[c0 + (int64_t)i * 16 * chunks_per_row] = o;
+    }
   }
   if (t == 0) sb[bn * nblk_k + bk] = s;
 }
+
+// Codes beyond the 256 MB Infinity Cache cannot stay cached for the kernel
+// that reads them next, so above that size both quantizers store them
+// non-temporally (same bytes; the streaming stores move HBM traffic faster).
+constexpr int64_t kCachedCodesMax = (int64_t)256 << 20;
 
 hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* q, float* sa,
                                   bool nontemporal, hipStream_t stream) {
   const int64_t n_tiles = M * (K / kGroup);
   const int64_t per_block = (int64_t)kActThreads * kActUnroll / 16;  // tiles per block
   const int64_t blocks = (n_tiles + per_block - 1) / per_block;
-  if (nontemporal)
+  if (nontemporal || M * K > kCachedCodesMax)
     hipLaunchKernelGGL(quant_act_1x128_kernel<true>, dim3((unsigned)blocks), dim3(kActThreads), 0,
                        stream, (const uint4*)x, (uint2*)q, sa, n_tiles);
   else
@@ -131,8 +144,12 @@ hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint
                                        hipStream_t stream) {
   const int nblk_k = (int)(K / kGroup);
   const int nblk_n = (int)(N / kGroup);
-  hipLaunchKernelGGL(quant_weight_128x128_kernel, dim3(nblk_k, nblk_n), dim3(kWThreads), 0, stream,
-                     (const uint4*)w, (uint2*)q, sb, K, nblk_k);
+  if (N * K > kCachedCodesMax)
+    hipLaunchKernelGGL(quant_weight_128x128_kernel<true>, dim3(nblk_k, nblk_n), dim3(kWThreads), 0, stream,
+                       (const uint4*)w, (uint2*)q, sb, K, nblk_k);
+  else
+    hipLaunchKernelGGL(quant_weight_128x128_kernel<false>, dim3(nblk_k, nblk_n), dim3(kWThreads), 0, stream,
+                       (const uint4*)w, (uint2*)q, sb, K, nblk_k);
   return hipGetLastError();
 }
 

@@ -90,6 +90,9 @@ FP8Q_API const char* fp8q_status_string(int status);
  *   q      : out, M x K E4M3 bytes, 16-byte aligned
  *   sa     : out, M x (K/128) float32, 4-byte aligned
  * Requires K % 128 == 0. M == 0 or K == 0 is a no-op returning FP8Q_OK.
+ * q and sa are written with ordinary stores, so a GEMM that reads them next
+ * finds them in the GPU's 256 MB Infinity Cache; codes larger than that cache
+ * (M * K > 256 MiB) cannot stay there and go out with non-temporal stores.
  */
 FP8Q_API int fp8q_quant_act_1x128(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* sa,
                          void* stream);
@@ -100,7 +103,8 @@ FP8Q_API int fp8q_quant_act_1x128(const void* x_bf16, int64_t M, int64_t K, uint
  * do not keep q and sa in the GPU's 256 MB Infinity Cache, which raises the
  * kernel's HBM throughput (16384 x 7168 on MI355X: 6.4 TB/s against 5.9).
  * Use it for activations that are not read next on this GPU (codes sent to
- * another GPU, or written out). For codes that a GEMM reads next, the cached
+ * another GPU, or written out); above 256 MiB of codes fp8q_quant_act_1x128
+ * stores this way by itself. For codes that a GEMM reads next, the cached
  * form is faster overall, because the GEMM then finds its operand in the
  * cache. (4096^3: quantization plus GEMM is about 11 us slower with
  * non-temporal codes.) Same source passages as fp8q_quant_act_1x128.
@@ -118,6 +122,7 @@ FP8Q_API int fp8q_quant_act_1x128_nt(const void* x_bf16, int64_t M, int64_t K, u
  *   q      : out, N x K E4M3 bytes
  *   sb     : out, (N/128) x (K/128) float32
  * Requires N % 128 == 0 and K % 128 == 0. N == 0 or K == 0 is a no-op.
+ * Store policy as for fp8q_quant_act_1x128: non-temporal when N * K > 256 MiB.
  */
 FP8Q_API int fp8q_quant_weight_128x128(const void* w_bf16, int64_t N, int64_t K, uint8_t* q, float* sb,
                               void* stream);

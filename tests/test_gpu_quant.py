@@ -135,3 +135,32 @@ def test_full_size_weights_sampled_blocks():
         r = slice(nb * 128, (nb + 1) * 128)
         wq, ws = quant.quant_weight_128x128(w[r])
         assert_same(q[r], sb[nb:nb + 1], wq, ws)
+
+
+def test_codes_beyond_the_cache_bit_exact():
+    """Above 256 MiB of codes both quantizers store non-temporally. A 4096-row
+    block repeated on the device to 40960 x 7168 activations and to
+    32 x 4096 x 7168 weights; sampled rows and blocks bit-exact against the
+    oracle on the host block they repeat."""
+    import fp8_fine_grained_online_amd as F
+    import torch
+    from oracle import quant
+    K = 7168
+    x = S.activations(4096, K, S.rng_for(730, 0))
+    q, sa = F.fp8q_quant_act_1x128(to_dev_bf16(x).repeat(10, 1))
+    torch.cuda.synchronize()
+    assert q.shape[0] * K > 256 << 20
+    rows = np.array([0, 4095, 4096 + 17, 20000, 40959])
+    want_q, want_s = quant.quant_act_1x128(x[rows % 4096])
+    idx = torch.as_tensor(rows, device="cuda")
+    assert_same(q[idx].cpu().numpy(), sa[idx].cpu().numpy(), want_q, want_s)
+    del q, sa
+    w = S.weights(4096, K, S.rng_for(730, 1))
+    qb, sb = F.fp8q_quant_weight_128x128(to_dev_bf16(w).repeat(32, 1))
+    torch.cuda.synchronize()
+    assert qb.shape[0] * K > 256 << 20
+    for nb in [0, 31, 32 + 5, 1023]:
+        r = slice(nb * 128, (nb + 1) * 128)
+        h = slice((nb % 32) * 128, (nb % 32 + 1) * 128)
+        wq, ws = quant.quant_weight_128x128(w[h])
+        assert_same(qb[r].cpu().numpy(), sb[nb:nb + 1].cpu().numpy(), wq, ws)
