@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     }
     if (e == p.G) return;  // beyond the last real tile (grid is an upper bound)
     int tm;
-    band_tile(tile - before, te, n_tiles_n, tm, tile_n);
+    band_tile<kBandGrouped>(tile - before, te, n_tiles_n, tm, tile_n);
     m0 = lo + tm * BM;
     m_end = min(m0 + BM, hi);
     bmat += (int64_t)e * p.N * p.K;

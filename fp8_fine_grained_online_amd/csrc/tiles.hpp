@@ -46,13 +46,22 @@ __device__ __forceinline__ int xcd_tile(int id, int n) {
 // by column within a band: a run of 32 consecutive tiles (one XCD's share of
 // a wave of workgroups) is a 4 x 8 block that reads 4 A slabs and 8 B slabs,
 // instead of 2 x 16 (2 A + 16 B slabs) in plain row-major order.
+//
+// The grouped GEMM uses bands of kBandGrouped row tiles within each expert.
+// Its weights (all experts together) stream from HBM while an expert's rows
+// of A stay in the Infinity Cache, so a band as tall as a typical expert has
+// each weight panel read by all of the expert's row tiles in a row. Bands of
+// 16 (at most 4096 rows of A) beat bands of 4 by 4% on 32 experts of ~2100
+// rows, measured on MI355X.
 constexpr int kBand = 4;
+constexpr int kBandGrouped = 16;
+template <int kHeight = kBand>
 __device__ __forceinline__ void band_tile(int t, int m_tiles, int n_tiles, int& tm, int& tn) {
-  const int band = t / (kBand * n_tiles);
-  const int local = t - band * kBand * n_tiles;
-  const int h = min(kBand, m_tiles - band * kBand);  // rows in this (possibly last) band
+  const int band = t / (kHeight * n_tiles);
+  const int local = t - band * kHeight * n_tiles;
+  const int h = min(kHeight, m_tiles - band * kHeight);  // rows in this (possibly last) band
   tn = local / h;
-  tm = band * kBand + local % h;
+  tm = band * kHeight + local % h;
 }
 
 }  // namespace fp8q
