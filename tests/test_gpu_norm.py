@@ -42,10 +42,12 @@ def check(x, g, b, eps, centred):
     assert not dq.any(), f"{int(dq.sum())} codes differ; first {tuple(np.argwhere(dq)[0])}"
 
 
-# K = 128 .. 16384 covers the 2-, 4-, 8-, 16- and 32-chunk kernels, with
-# partially filled wavefronts (K = 128, 384, 7168 = 14 chunks per lane)
-@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (64, 1024), (33, 2048), (64, 7168),
-                                 (9, 8192), (7, 16384)])
+# K = 128 .. 16384 covers every instantiated row size (2, 4, 6, 8, 10, 12, 14,
+# 16, 20, 24, 28 and 32 chunks per lane), with partially filled wavefronts
+# (K = 128, 384, 2944)
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 384), (64, 1024), (33, 2048), (6, 2944), (5, 3072),
+                                 (4, 4096), (3, 5120), (4, 6144), (64, 7168), (9, 8192),
+                                 (3, 10240), (2, 12288), (2, 14336), (7, 16384)])
 @pytest.mark.parametrize("centred", [False, True])
 def test_shapes(M, K, centred):
     x = S.activations(M, K, S.rng_for(980 + M, K))
