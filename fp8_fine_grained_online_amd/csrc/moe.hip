@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kMaxExperts) void dispatch_scan_kernel(
   }
   __syncthreads();
   // expert totals (thread p = 0 of each expert), then an inclusive scan of the
-  // padded totals over all 1024 threads (Hillis-Steele in LDS)
+  // padded totals (Hillis-Steele in LDS; entries from G on are zero, so steps
+  // d < G give every expert's full prefix)
   __shared__ int32_t scan[kMaxExperts];
   int padded = 0;
   if (on && p == 0) {
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kMaxExperts) void dispatch_scan_kernel(
   __syncthreads();
   if (slot_e >= 0) scan[slot_e] = padded;
   __syncthreads();
-  for (int d = 1; d < kMaxExperts; d <<= 1) {
+  for (int d = 1; d < G; d <<= 1) {
     const int v = tid >= d ? scan[tid - d] : 0;
     __syncthreads();
     scan[tid] += v;
@@ -97,11 +98,19 @@ __global__ __launch_bounds__(kMaxExperts) void dispatch_scan_kernel(
   if (on) {
     int run = off[e];
     for (int q = 0; q < p; ++q) run += part[e * tpe + q];
-    for (int b = b0; b < b1; ++b) {
-      const int64_t i = (int64_t)b * G + e;
-      const int c = hist[i];
-      base[i] = run;
-      run += c;
+    // eight blocks at a time: their loads are issued together instead of one
+    // memory latency per block
+    for (int b = b0; b < b1; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = (b + j < b1) ? hist[(int64_t)(b + j) * G + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b + j < b1) {
+          base[(int64_t)(b + j) * G + e] = run;
+          run += c[j];
+        }
+      }
     }
   }
 }
