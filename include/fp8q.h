@@ -163,9 +163,10 @@ FP8Q_API int fp8_gemm_blockscaled(const uint8_t* a, const float* sa, const uint8
  *     fp8_gemm_blockscaled_ws_bytes(M, N, K) bytes, 16-byte aligned, owned by
  *     the caller, no contents needed on entry. When that size is 0 the shape
  *     does not take the split path and the call is fp8_gemm_blockscaled
- *     (workspace may then be NULL). The size is 4 * S * M * N for S splits
- *     (S <= 256 / number of 64 x 128 tiles). Two calls in flight at once on
- *     one workspace (different streams) race.
+ *     (workspace may then be NULL): shapes with fewer than 16 K groups
+ *     (K < 2048), or too many tiles for two splits. The size is 4 * S * M * N
+ *     for S splits (S <= 256 / number of 64 x 128 tiles). Two calls in flight
+ *     at once on one workspace (different streams) race.
  */
 FP8Q_API int fp8_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const uint8_t* b,
                                      const float* sb, void* c, int out_dtype, int64_t M, int64_t N,
