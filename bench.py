@@ -155,7 +155,7 @@ def copy_calibration(steps, warmup):
 
 
 def read_sclk():
-    """The GPU's current shader-clock level as the driver reports it
+    """The GPU's current shader-clock level as the amdgpu driver reports it
     (pp_dpm_sclk of the device's PCI node), or None where it is not readable."""
     import torch
     try:
@@ -605,7 +605,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
-    sclk = []  # the driver's clock level, read on the host while steps run
+    sclk = []  # the amdgpu driver's clock level, read on the host while steps run
     for i in range(args.steps):
         step(evs[i])
         sclk.append(read_sclk())
