@@ -52,8 +52,11 @@ def check_against_oracle(x, ids, G):
     assert np.all(qh[M:] == POISON) and np.all(np.isnan(sah[M:]))  # not written
 
 
+# K up to 8192 keeps a token's codes in registers and writes each destination
+# row in one pass (8192: 8 steps, the limit); larger K stores step by step
 @pytest.mark.parametrize("T,k,G,K", [(64, 8, 32, 256), (300, 2, 7, 384), (129, 1, 1, 128),
-                                     (50, 6, 256, 128), (1000, 8, 32, 1024), (257, 3, 1024, 128)])
+                                     (50, 6, 256, 128), (1000, 8, 32, 1024), (257, 3, 1024, 128),
+                                     (40, 4, 16, 8192), (33, 3, 8, 9216), (20, 2, 4, 16384)])
 def test_small(T, k, G, K):
     x = S.activations(T, K, S.rng_for(1000 + T, K))
     check_against_oracle(x, routing(T, k, G, 1001 + T, drop_every=7), G)
