@@ -287,3 +287,26 @@ def test_split_k_full_size_64x7168x7168_sampled_columns():
     from oracle import bf16
     want = gemm.round_bf16(c64)
     check_bf16(got[:, cols], c64, S_, T, want, bf16.ulp(want))
+
+
+def test_calls_run_on_the_callers_stream():
+    """The binding passes torch's current stream to the C ABI and the kernels
+    run there: with the default stream held busy by a bounded spin, the
+    quantizers and the GEMM issued on a side stream finish and are read back
+    on that stream, while the default stream is still spinning."""
+    import fp8_fine_grained_online_amd as F
+    import torch
+    a = S.activations(256, 512, S.rng_for(890, 0))
+    b = S.weights(256, 512, S.rng_for(890, 1))
+    want = gpu_pipeline(a, b, "f32")  # default stream, synchronized
+    xa, xb = to_dev_bf16(a), to_dev_bf16(b)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    torch.cuda._sleep(1 << 27)  # the default stream spins (2^27 clock ticks: tens of ms or more)
+    with torch.cuda.stream(side):
+        qa, sa = F.fp8q_quant_act_1x128(xa)
+        qb, sb = F.fp8q_quant_weight_128x128(xb)
+        c = F.fp8_gemm_blockscaled(qa, sa, qb, sb, "f32", c=poisoned((256, 256), torch.float32))
+        got = c.cpu().numpy()  # copy on the side stream, ordered after the GEMM only
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
