@@ -310,3 +310,54 @@ def test_calls_run_on_the_callers_stream():
         got = c.cpu().numpy()  # copy on the side stream, ordered after the GEMM only
     torch.cuda.synchronize()
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_forward_step_in_a_hip_graph():
+    """The library allocates nothing and sets no memory, so its calls can be
+    captured: the forward step (both quantizers and the GEMM, into fixed
+    buffers) captured once in a HIP graph and replayed on new inputs, with
+    eager copies and synchronizations between the replays, matches eager
+    calls bit for bit on every replay."""
+    import fp8_fine_grained_online_amd as F
+    import torch
+    M, N, K = 512, 768, 1024
+    xa = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    xb = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N // 128, K // 128), device="cuda")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        F.fp8q_quant_act_1x128(xa, q=qa, sa=sa)
+        F.fp8q_quant_weight_128x128(xb, q=qb, sb=sb)
+        F.fp8_gemm_blockscaled(qa, sa, qb, sb, "bf16", c=c)
+
+    def load(r):
+        xa.copy_(to_dev_bf16(S.activations(M, K, S.rng_for(895, r))))
+        xb.copy_(to_dev_bf16(S.weights(N, K, S.rng_for(896, r))))
+
+    load(0)
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(1, 4):
+        load(r)
+        torch.cuda.synchronize()
+        step()  # eager
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (qa, sa, qb, sb, c)]
+        for t in (qa, sa, qb, sb, c):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((qa, sa, qb, sb, c), want):
+            assert torch.equal(got.view(torch.uint8), exp.view(torch.uint8)), r
