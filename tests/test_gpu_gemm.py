@@ -174,15 +174,16 @@ def gpu_grouped(a_bits, b_bits, off, out):
     return c
 
 
-@pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_grouped_small_with_empty_experts_and_padding(out):
+def grouped_case(counts, N, K, seed, out):
+    """Every output of a grouped GEMM (token counts per expert, each padded to
+    128 rows) against the oracle."""
     from oracle import gemm, quant
-    counts = np.array([100, 0, 300, 128, 1, 0])
+    counts = np.asarray(counts)
     padded = (counts + 127) // 128 * 128
     off = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
-    G, N, K = len(counts), 256, 512
-    a = S.moe_activations(counts, off, K, S.rng_for(840, 0))
-    b = np.stack([S.weights(N, K, S.rng_for(840, 1 + e)) for e in range(G)])
+    G = len(counts)
+    a = S.moe_activations(counts, off, K, S.rng_for(seed, 0))
+    b = np.stack([S.weights(N, K, S.rng_for(seed, 1 + e)) for e in range(G)])
     c = gpu_grouped(a, b, off, out)
     got = from_dev_bf16_bits(c) if out == "bf16" else c.cpu().numpy()
     qa, sa = quant.quant_act_1x128(a)
@@ -196,6 +197,18 @@ def test_grouped_small_with_empty_experts_and_padding(out):
         if off[e + 1] > off[e]:
             T[r] = mfma_bound(qa[r], sa[r], qb[e], sb[e])
     check(got, c64, S_, T, out)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_grouped_small_with_empty_experts_and_padding(out):
+    grouped_case([100, 0, 300, 128, 1, 0], 256, 512, 840, out)
+
+
+def test_grouped_experts_taller_than_a_band():
+    """Tiles go in bands of 16 row tiles within an expert: experts of 17 and
+    33 row tiles (a partial last band, two full bands), an empty one and a
+    one-tile one, with a half-filled last column tile (N = 384)."""
+    grouped_case([4300, 0, 8400, 37], 384, 256, 841, "f32")
 
 
 def test_grouped_full_size_sampled_experts():
