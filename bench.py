@@ -37,6 +37,7 @@ MALL_BYTES = 256 << 20     # MI355X Infinity Cache
 # sources whose hash keys the recorded counters of each streaming kernel
 STREAM_SOURCES = {"quant_act_1x128": ("quant.hip", "common.hpp"),
                   "quant_act_1x128_nt": ("quant.hip", "common.hpp"),
+                  "quant_weight_128x128": ("quant.hip", "common.hpp"),
                   "norm_quant_act_1x128": ("norm.hip", "common.hpp"),
                   "moe_dispatch_1x128": ("moe.hip", "common.hpp")}
 
@@ -357,6 +358,22 @@ def plan_stream(w, args, F, S, L, dev, sp, up_bf16):
     import torch
     from fp8_fine_grained_online_amd.synthetic import T_B
     M, K = w.M, w.K
+    if w.name.startswith("wquant"):
+        # weights (N(0, 0.02)), 128x128 blocks: M x K codes, (M/128) x (K/128) scales
+        x_bits = S.weights(M, K, S.rng_for(w.wid, T_B, args.seed))
+        X = up_bf16(x_bits)
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sb = torch.empty((M // 128, K // 128), dtype=torch.float32, device=dev)
+        nbytes = M * K * 3 + (M // 128) * (K // 128) * 4
+        name = "quant_weight_128x128"
+        fn = lambda: L.fp8q_quant_weight_128x128(X.data_ptr(), M, K, q.data_ptr(), sb.data_ptr(), sp)
+        cpu = lambda: cpu_baseline_weights(args.workload, x_bits, nbytes / M, 4096)
+        return {
+            "launches": [(name, fn)], "flops": {}, "bytes": {name: nbytes}, "stream": name,
+            "config": {"workload": args.workload, "M": M, "K": K, "step": name,
+                       "bytes_per_step": nbytes},
+            "extra": {}, "cpu": cpu,
+        }
     x_bits, _ = S.dense_inputs(w, args.seed)
     X = up_bf16(x_bits)
     q = torch.empty((M, K), dtype=torch.uint8, device=dev)
@@ -472,6 +489,22 @@ def cpu_baseline_stream(workload, x_bits, bytes_per_row, rows, gamma_bits):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{workload}: oracle {what} of the first {rows} rows; {dt:.2f} s",
+    }
+
+
+def cpu_baseline_weights(workload, w_bits, bytes_per_row, rows):
+    """The oracle, untuned, on the first `rows` rows (whole 128x128 blocks)."""
+    from oracle import quant
+    threads = oracle_threads()
+    t0 = time.perf_counter()
+    quant.quant_weight_128x128(w_bits[:rows])
+    dt = time.perf_counter() - t0
+    return {
+        "value": bytes_per_row * rows / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{workload}: oracle 128x128 quantization of the first {rows} rows; {dt:.2f} s",
     }
 
 

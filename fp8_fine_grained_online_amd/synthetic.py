@@ -102,6 +102,9 @@ WORKLOADS = {
     "skinny_64x7168x7168": Workload(30, "skinny_64x7168x7168", 64, 7168, 7168),
     "actquant_16384x7168": Workload(31, "actquant_16384x7168", 16384, 0, 7168),
     "normquant_16384x7168": Workload(32, "normquant_16384x7168", 16384, 0, 7168),
+    # standalone 128x128 weight quantization: 32 experts' 4096 x 7168 weights as
+    # one 131072 x 7168 tensor
+    "wquant_32x4096x7168": Workload(35, "wquant_32x4096x7168", 32 * 4096, 0, 7168),
     "dispatch_8192x7168_top8_g32": Workload(33, "dispatch_8192x7168_top8_g32", 8192, 0, 7168,
                                             G=32, topk=8),
     "moe_up_8192x4096x7168_top8_g32": Workload(34, "moe_up_8192x4096x7168_top8_g32", 8192, 4096,

@@ -42,6 +42,8 @@ def test_cpu_baseline_legs_on_tiny_inputs():
     check_baseline(bench.cpu_baseline("tiny", a, b, 128))
     dy = S.activations(256, 128, S.rng_for(990, 2))
     check_baseline(bench.cpu_baseline_backward("tiny", a, b, dy, 64))
+    d = bench.cpu_baseline_weights("tiny", b, 256 * 3.0, 128)
+    assert d["unit"] == "GB/s" and d["kind"] == "oracle" and d["value"] > 0
     g, _ = S.norm_params(256, S.rng_for(990, 3))
     for gamma in (None, g):
         d = bench.cpu_baseline_stream("tiny", a, 256 * 3.03, 64, gamma)
