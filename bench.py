@@ -367,7 +367,7 @@ def plan_stream(w, args, F, S, L, dev, sp, up_bf16):
         nbytes = M * K * 3 + (M // 128) * (K // 128) * 4
         name = "quant_weight_128x128"
         fn = lambda: L.fp8q_quant_weight_128x128(X.data_ptr(), M, K, q.data_ptr(), sb.data_ptr(), sp)
-        cpu = lambda: cpu_baseline_weights(args.workload, x_bits, nbytes / M, 4096)
+        cpu = lambda: cpu_baseline_weights(args.workload, x_bits, nbytes / M, 32768)  # 8 experts
         return {
             "launches": [(name, fn)], "flops": {}, "bytes": {name: nbytes}, "stream": name,
             "config": {"workload": args.workload, "M": M, "K": K, "step": name,
