@@ -232,9 +232,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   // first kCopyOff MFMAs: until then every wave's B-fragment reads are being
   // served, and a copy's LDS write would compete with them for LDS bandwidth.
   // Measured on MI355X at three shapes, one copy every 2 MFMAs from MFMA 3
-  // beats one every 3 from MFMA 0 by 1-4%.
+  // beats one every 3 from MFMA 0 by 1-4%. The grouped GEMM, whose weights
+  // come from HBM rather than the Infinity Cache, does best with its copies
+  // one per MFMA from MFMA 3 (32-expert MoE: 2227 against 2262 us).
   constexpr int kCopyOff = 3;
-  constexpr int kCopyEvery = 2;
+  constexpr int kCopyEvery = kGrouped ? 1 : 2;
   static_assert(kCopyOff + (kCopies - 1) * kCopyEvery < SUBM * SUBN, "the copies fit in a step");
   // acc += part * scale: one scale for the lane's four columns (128x128 B
   // blocks: sc1 = sa * sb), or one per column (kRowB: sa * sb_row, formed
