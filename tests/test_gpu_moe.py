@@ -54,9 +54,13 @@ def check_against_oracle(x, ids, G):
 
 # K up to 8192 keeps a token's codes in registers and writes each destination
 # row in one pass (8192: 8 steps, the limit); larger K stores step by step
+# The last three rows give the offsets scan several 256-slot blocks per thread
+# with ragged runs (305 and 625 blocks over 64 threads per expert) and, at
+# G = 600, ten experts per lane in the prefix over the experts' totals.
 @pytest.mark.parametrize("T,k,G,K", [(64, 8, 32, 256), (300, 2, 7, 384), (129, 1, 1, 128),
                                      (50, 6, 256, 128), (1000, 8, 32, 1024), (257, 3, 1024, 128),
-                                     (40, 4, 16, 8192), (33, 3, 8, 9216), (20, 2, 4, 16384)])
+                                     (40, 4, 16, 8192), (33, 3, 8, 9216), (20, 2, 4, 16384),
+                                     (26000, 3, 3, 128), (40000, 4, 6, 128), (3000, 8, 600, 128)])
 def test_small(T, k, G, K):
     x = S.activations(T, K, S.rng_for(1000 + T, K))
     check_against_oracle(x, routing(T, k, G, 1001 + T, drop_every=7), G)
