@@ -114,8 +114,8 @@ FP8Q_API int fp8q_quant_act_1x128_nt(const void* x_bf16, int64_t M, int64_t K, u
 
 /*
  * 128x128 weight quantization: as above with amax over each 128x128 block.
- * Source: the Figure 7 (a) passage ("per 128 input channels per 128 output
- * channels") of "Six Reasons Deepseek Ai Is A Waste Of Time".
+ * Source: the Figure 7 (a) passage of "Six Reasons Deepseek Ai Is A Waste Of
+ * Time" (weights grouped in blocks of 128 input by 128 output channels).
  *
  *   w_bf16 : in,  N x K bfloat16 (for G experts pass N = G * N_e: the blocks
  *            never straddle experts when N_e % 128 == 0)
