@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "block-scaled FP8 GEMM TFLOPS & % of FP8 MFMA peak (4096^3, grouped MoE)"
+DEFAULT_WORKLOAD = "dense_4096x4096x4096"
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MALL_BYTES = 256 << 20     # MI355X Infinity Cache
@@ -68,6 +69,24 @@ def measured_traffic(workload, kernel_src):
     if not rec or rec.get("source_hash") != source_hash(*kernel_src):
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_mfma(workload, kernel_src, path=None):
+    """MFMA-unit counters of the roofline kernel from committed rocprofv3 --pmc
+    runs (profiles/mfma_counters.json), if the kernel's source is unchanged:
+    mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES over the cycles the chip's SIMDs could
+    have kept the matrix units busy during the kernel, and the FP8 MFMA FLOP
+    the counters saw per launch."""
+    path = path or os.path.join(ROOT, "profiles", "mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(*kernel_src):
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "mfma_flop_per_launch") if k in rec}
 
 
 def oracle_threads():
@@ -153,23 +172,6 @@ def copy_calibration(steps, warmup):
     n, ms = copy_rate(steps, warmup)
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 5),
                       "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
-
-
-def read_sclk():
-    """The GPU's current shader-clock level as the amdgpu driver reports it
-    (pp_dpm_sclk of the device's PCI node), or None where it is not readable."""
-    import torch
-    try:
-        pr = torch.cuda.get_device_properties(0)
-        node = "/sys/bus/pci/devices/%04x:%02x:%02x.0/pp_dpm_sclk" % (
-            pr.pci_domain_id, pr.pci_bus_id, pr.pci_device_id)
-        with open(node) as f:
-            for line in f:
-                if line.rstrip().endswith("*"):
-                    return line.split(":", 1)[1].strip().rstrip("*").strip()
-    except (AttributeError, OSError, ValueError, IndexError, RuntimeError):
-        pass
-    return None
 
 
 def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
@@ -271,6 +273,53 @@ def plan_forward(w, args, F, S, L, dev, sp, up_bf16):
                  if gemm_name == "fp8_gemm_blockscaled" and M >= 256 and N >= 256 and K == 4096
                  else None,
     }
+
+
+def grouped_moe_line(args, F, S, L, dev, sp, up_bf16, steps, warmup):
+    """The grouped half of the headline metric: the 32-expert MoE GEMM
+    (65536 tokens, N = 4096, K = 7168, bf16 out) timed on its own after its
+    operands are quantized once. TFLOP/s over the real tokens (the algorithmic
+    count) and over the padded rows; fraction of the FP8 MFMA peak."""
+    import torch
+    name = "moe_g32_65536x4096x7168"
+    w = S.WORKLOADS[name]
+    sub = argparse.Namespace(**dict(vars(args), workload=name))
+    plan = plan_forward(w, sub, F, S, L, dev, sp, up_bf16)
+    launches = dict(plan["launches"])
+    for n in ("quant_act_1x128", "quant_weight_128x128"):
+        if launches[n]():
+            raise RuntimeError(f"{n} failed")
+    gemm = launches["fp8_gemm_grouped"]
+    for _ in range(warmup):
+        gemm()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    st = 0
+    for _ in range(steps):
+        st |= gemm()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    if st:
+        raise RuntimeError(f"fp8_gemm_grouped failed with status {st}")
+    ms = t0.elapsed_time(t1) / steps
+    real = plan["flops"]["fp8_gemm_grouped"] / (ms * 1e-3) / 1e12
+    padded = plan["extra"]["gemm_tflops_padded"][1] / (ms * 1e-3) / 1e12
+    src = ("gemm.hip", "tiles.hpp", "common.hpp")
+    out = {"workload": name, "kernel": "fp8_gemm_grouped", "kernel_ms": round(ms, 5),
+           "steps": steps, "tokens": w.tokens, "rows_padded": plan["config"]["M"],
+           "tflops": round(real, 2), "frac": round(real / FP8_PEAK_TFLOPS, 4),
+           "tflops_padded": round(padded, 2), "peak": FP8_PEAK_TFLOPS,
+           "traffic": measured_traffic(name, src)}
+    counters = measured_mfma(name, src)
+    if counters:
+        out.update(counters)
+    del plan, launches, gemm
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 def accumulation_demo(a_bits, b_bits, gpu_corner, n=256):
@@ -542,7 +591,9 @@ def main():
     # the clock takes a few hundred microseconds of load to settle: the default
     # warms up long enough for the short steps too
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="dense_4096x4096x4096")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="skip the grouped MoE GEMM line that the default workload also reports")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -638,13 +689,9 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
-    sclk = []  # the amdgpu driver's clock level, read on the host while steps run
     for i in range(args.steps):
         step(evs[i])
-        sclk.append(read_sclk())
     torch.cuda.synchronize()
-    mhz = [int(v.lower().replace("mhz", "")) for v in sclk if v and v.lower().endswith("mhz")
-           and v[:-3].isdigit()]
     per_launch = {n: np.array([e[i].elapsed_time(e[i + 1]) for e in evs]) for i, n in enumerate(names)}
     kms = {n: float(v.mean()) for n, v in per_launch.items()}
     kpct = {n: [round(float(x), 5) for x in np.percentile(v, [10, 50, 90])]
@@ -685,6 +732,9 @@ def main():
             roofline = {"bound": "mfma", "kernel": gemm_name, "achieved": round(gemm_tflops, 2),
                         "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic}
+            counters = measured_mfma(args.workload, gemm_src)
+            if counters:
+                roofline.update(counters)
 
     out = {
         "metric": metric,
@@ -704,8 +754,6 @@ def main():
         "roofline": roofline,
         "kernels_ms": {n: round(v, 5) for n, v in kms.items()},
         "kernels_ms_p10_p50_p90": kpct,
-        "sclk_driver_mhz": ({"median": int(np.median(mhz)), "max": max(mhz), "samples": len(mhz)}
-                            if mhz else None),
         "kernels_GBps": {n: round(b / (kms[n] * 1e-3) / 1e9, 1) for n, b in plan["bytes"].items()},
         "kernels_TFLOPs": {n: round(f / (kms[n] * 1e-3) / 1e12, 2) for n, f in plan["flops"].items()},
         "wall_s_timed": round(wall, 4),
@@ -719,10 +767,17 @@ def main():
         copy_gbps = 2 * n_copy / (ms_copy * 1e-3) / 1e9
         roofline["copy_GBps"] = round(copy_gbps, 1)
         roofline["frac_of_copy"] = round(roofline["achieved"] / copy_gbps, 4)
+    cpu_fn, accum_fn = plan["cpu"], plan.get("accum")
+    if args.workload == DEFAULT_WORKLOAD and not args.no_grouped:
+        # the metric names both the 4096^3 GEMM and the grouped MoE GEMM
+        del copies, plan
+        out["grouped_moe"] = grouped_moe_line(args, F, S, L, dev, sp, up_bf16,
+                                              steps=max(5, min(args.steps, 50)),
+                                              warmup=max(3, min(args.warmup, 20)))
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = plan["cpu"]()
-        if plan.get("accum"):
-            out["accumulation_demo"] = plan["accum"]()
+        out["cpu_baseline"] = cpu_fn()
+        if accum_fn:
+            out["accumulation_demo"] = accum_fn()
     print(json.dumps(out), flush=True)
 
 

@@ -261,6 +261,26 @@ def fp8_gemm_blockscaled_ws(a, sa, b, sb, out_dtype="bf16", c=None, workspace=No
     return c
 
 
+def _grouped_shapes(a, sa, b, sb, m_offsets, M_total):
+    """Shape checks of the grouped GEMM's operands (before any device access):
+    the kernel indexes expert e's block scales at sb + e * (N/128) * (K/128), so
+    sb must be exactly G x N/128 x K/128 for the b it goes with."""
+    if b.dim() != 3 or a.dim() != 2 or sa.dim() != 2 or sb.dim() != 3 or m_offsets.dim() != 1:
+        raise ValueError("a, sa: 2 dims; b, sb: 3 dims; m_offsets: 1 dim")
+    G, N, K = b.shape
+    if m_offsets.shape[0] != G + 1:
+        raise ValueError("m_offsets must have G+1 entries")
+    M = a.shape[0] if M_total is None else int(M_total)
+    if a.shape[1] != K or a.shape[0] < M:
+        raise ValueError("a must be at least M_total x K")
+    if K % 128 == 0 and N % 128 == 0:
+        if sa.shape[0] < M or sa.shape[1] != K // 128:
+            raise ValueError("sa must be at least M_total x K/128")
+        if tuple(sb.shape) != (G, N // 128, K // 128):
+            raise ValueError(f"sb must have shape {(G, N // 128, K // 128)}, got {tuple(sb.shape)}")
+    return G, N, K, M
+
+
 def fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype="bf16", c=None, M_total=None, stream=None):
     """Grouped GEMM. b: G x N x K codes, sb: G x N/128 x K/128, m_offsets: int32[G+1] device.
 
@@ -269,19 +289,12 @@ def fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype="bf16", c=None, M_total=
     """
     torch = _torch()
     code, tdt = _out_dtype(out_dtype)
+    G, N, K, M = _grouped_shapes(a, sa, b, sb, m_offsets, M_total)
     pa = _dev(a, "a", torch.uint8, 2)
     psa = _dev(sa, "sa", torch.float32, 2)
     pb = _dev(b, "b", torch.uint8, 3)
     psb = _dev(sb, "sb", torch.float32, 3)
     poff = _dev(m_offsets, "m_offsets", torch.int32, 1)
-    G, N, K = b.shape
-    if m_offsets.shape[0] != G + 1:
-        raise ValueError("m_offsets must have G+1 entries")
-    M = a.shape[0] if M_total is None else int(M_total)
-    if a.shape[1] != K or a.shape[0] < M:
-        raise ValueError("a must be at least M_total x K")
-    if K % 128 == 0 and (sa.shape[0] < M or sa.shape[1] != K // 128):
-        raise ValueError("sa must be at least M_total x K/128")
     c = _out(c, "c", (M, N), tdt, a.device)
     _check("fp8_gemm_grouped",
            lib().fp8_gemm_grouped(pa, psa, pb, psb, c.data_ptr(), code, poff, G, M, N, K,

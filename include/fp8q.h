@@ -261,7 +261,9 @@ FP8Q_API int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* 
  *                 fp8q_moe_dispatch_workspace_bytes(T, topk, G) bytes, 4-byte
  *                 aligned, owned by the caller; no contents needed on entry
  * Requires K % 128 == 0, topk >= 1, 1 <= G <= 1024. T == 0 still writes
- * m_offsets (all zero). Five kernels are enqueued on `stream`.
+ * m_offsets (all zero). Up to four kernels are enqueued on `stream`: count,
+ * scan, rank and quantize/scatter (no count or rank kernel when T == 0, no
+ * quantize/scatter kernel when K == 0).
  */
 FP8Q_API int fp8q_moe_dispatch_1x128(const void* x_bf16, const int32_t* topk_ids, int64_t T,
                                      int64_t K, int64_t topk, int64_t G, uint8_t* q, float* sa,

@@ -24,3 +24,18 @@ def gpu_available() -> bool:
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the GEMM parity statistics the GPU tests recorded, if asked to."""
+    path = os.environ.get("FP8Q_PARITY_REPORT")
+    if not path:
+        return
+    try:
+        import helpers
+    except ImportError:
+        return
+    if helpers.PARITY_STATS:
+        import json
+        with open(path, "w") as f:
+            json.dump(helpers.PARITY_STATS, f, indent=1)

@@ -1,11 +1,13 @@
 """C-ABI checks that need no GPU: the library loads, exports every declared
 entry point, and rejects bad arguments on the host before any HIP call.
 
-The calls pass fake device addresses and count on stopping at validation or,
-for valid arguments, at the device check (FP8Q_ERR_NO_DEVICE). On a machine
-with a GPU a valid call would launch its kernels on those addresses, so the
-module runs only where no GPU is present; the GPU suites exercise the same
-entry points with real buffers."""
+Every call here either fails validation (a status other than FP8Q_OK, returned
+before the first HIP call) or is a zero-size no-op that returns FP8Q_OK before
+the first HIP call. No call carries arguments that pass validation, so none
+can reach a kernel launch on the fake addresses it passes, on any machine. As
+a second guard the module still skips itself where a GPU is visible (torch
+sees one, or the kernel driver's device node exists); the GPU suites exercise
+every entry point with real buffers."""
 
 import ctypes
 import os
@@ -15,7 +17,7 @@ import pytest
 
 from conftest import ROOT, gpu_available
 
-pytestmark = pytest.mark.skipif(gpu_available(),
+pytestmark = pytest.mark.skipif(gpu_available() or os.path.exists("/dev/kfd"),
                                 reason="fake device addresses: runs only without a GPU")
 
 HEADER = os.path.join(ROOT, "include", "fp8q.h")
@@ -113,7 +115,7 @@ def test_gemm_validation():
     assert f(A, SA, B, SB + 2, C, 0, 64, 128, 128, None) == 3
     assert f(A, SA, B, SB, C, 0, 1 << 31, 128, 128, None) == 7
     assert f(A, SA, B, SB, C, 0, 64, 128, (1 << 23) + 128, None) == 7  # K limit
-    assert f(A, SA, B, SB, C, 0, 64, 128, 1 << 23, None) == 6  # the largest K passes validation
+    assert f(A + 8, SA, B, SB, C, 0, 64, 128, 1 << 23, None) == 3  # the largest K gets past the size checks
     assert f(None, None, None, None, None, 0, 0, 128, 128, None) == 0
     assert f(None, None, None, None, None, 0, 64, 0, 128, None) == 0
 
@@ -229,10 +231,11 @@ def test_dispatch_sizes_and_validation():
         assert call(**{name: None}) == 1, name
     assert call(x=X + 8) == 3 and call(q=Q + 4) == 3 and call(ids=SB + 2) == 3
     assert call(sa=SA + 2) == 3 and call(off=OFFS + 2) == 3 and call(ws=WS + 2) == 3
-    # T = 0 needs no token pointers and passes validation (it still writes
-    # m_offsets; with real buffers: test_gpu_moe.py::test_no_tokens_writes_zero_offsets)
+    # T = 0 needs no token pointers: with a misaligned m_offsets it reaches the
+    # alignment check (valid T = 0 calls still write m_offsets; with real
+    # buffers: test_gpu_moe.py::test_no_tokens_writes_zero_offsets)
     assert call(T=0, x=None, ids=None, rows=None, cap=L.fp8q_moe_dispatch_max_rows(0, 2, 4),
-                wsb=L.fp8q_moe_dispatch_workspace_bytes(0, 2, 4)) == 6
+                wsb=L.fp8q_moe_dispatch_workspace_bytes(0, 2, 4), off=OFFS + 2) == 3
 
 
 def test_gemm_ws_validation():
@@ -263,9 +266,10 @@ def test_quant_on_load_gemm_validation():
     assert f(X, B, SB, C, 1, 64, 128, 128, Q + 8, SA, None) == 3
     assert f(X, B, SB, C, 1, 64, 128, (1 << 23) + 128, None, None, None) == 7
     assert f(None, None, None, None, 1, 0, 128, 128, None, None, None) == 0
-    # K == 0 reads no operand and passes validation (it zero-fills C; with a
-    # real C: test_gpu_gemm_qa.py::test_k_zero_writes_zeros_and_m_zero_is_a_no_op)
-    assert f(None, None, None, C, 1, 64, 128, 0, None, None, None) == 6
+    # K == 0 reads no operand: without A, B and sb it reaches the check of C
+    # (valid K = 0 calls zero-fill C; with a real C:
+    # test_gpu_gemm_qa.py::test_k_zero_writes_zeros_and_m_zero_is_a_no_op)
+    assert f(None, None, None, C + 8, 1, 64, 128, 0, None, None, None) == 3
 
 
 def test_rowscaled_gemm_validation():
@@ -281,24 +285,6 @@ def test_rowscaled_gemm_validation():
     assert f(A, SA, B, SB + 2, C, 0, 64, 128, 128, None) == 3
     assert f(A, SA, B, SB, C, 0, 64, 128, (1 << 23) + 128, None) == 7
     assert f(None, None, None, None, None, 0, 0, 128, 128, None) == 0
-
-
-def test_valid_call_without_gpu_reports_no_device():
-    L = _lib()
-    assert L.fp8q_quant_act_1x128(X, 4, 128, Q, SA, None) == 6
-    assert L.fp8q_quant_act_1x128_nt(X, 4, 128, Q, SA, None) == 6
-    assert L.fp8_gemm_blockscaled(A, SA, B, SB, C, 1, 64, 128, 128, None) == 6
-    assert L.fp8_gemm_blockscaled_bf16a(X, B, SB, C, 1, 64, 128, 128, Q, SA, None) == 6
-    assert L.fp8q_quant_act_128x1(X, 128, 128, Q, SB, None) == 6
-    assert L.fp8q_quant_act_1x128_128x1(X, 128, 128, Q, SA, B, SB, None) == 6
-    assert L.fp8q_norm_quant_act_1x128(X, B, None, 1e-6, 0, 4, 128, Q, SA, None) == 6
-    assert L.fp8_gemm_blockscaled_ws(A, SA, B, SB, C, 1, 64, 7168, 7168, P * 9,
-                                     L.fp8_gemm_blockscaled_ws_bytes(64, 7168, 7168), None) == 6
-    assert L.fp8q_moe_dispatch_1x128(X, SB, 64, 256, 2, 4, Q, SA, 640, OFF, A, C,
-                                     L.fp8q_moe_dispatch_workspace_bytes(64, 2, 4), None) == 6
-    assert L.fp8q_requant_1x128_to_128x1(X, SA, 128, 128, Q, SB, None) == 6
-    assert L.fp8q_transpose_weight_128x128(X, SA, 128, 128, Q, SB, None) == 6
-    assert L.fp8_gemm_rowscaled(A, SA, B, SB, C, 0, 64, 128, 128, None) == 6
 
 
 def test_binding_names_match_c_abi():

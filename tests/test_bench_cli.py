@@ -71,11 +71,20 @@ def test_backward_workload_inputs_have_the_layer_shapes():
     assert x.dtype == wt.dtype == dy.dtype == np.uint16
 
 
-def test_sclk_reader_never_raises():
-    """Without a readable clock node (here: no GPU at all) the JSON field is null."""
+def test_counter_records_are_keyed_by_source(tmp_path):
+    """Recorded MFMA counters are reported only for the kernel source they were
+    taken on: a record whose source hash differs from the current source gives
+    null, as does a workload with no record."""
+    import json
     import bench
-    v = bench.read_sclk()
-    assert v is None or isinstance(v, str)
+    src = ("gemm.hip", "tiles.hpp", "common.hpp")
+    path = str(tmp_path / "mfma_counters.json")
+    json.dump({"w_cur": {"source_hash": bench.source_hash(*src), "mfma_busy": 0.5,
+                         "mfma_flop_per_launch": 1.0},
+               "w_old": {"source_hash": "0" * 16, "mfma_busy": 0.5}}, open(path, "w"))
+    assert bench.measured_mfma("w_cur", src, path) == {"mfma_busy": 0.5, "mfma_flop_per_launch": 1.0}
+    assert bench.measured_mfma("w_old", src, path) is None
+    assert bench.measured_mfma("no_such_workload", src, path) is None
 
 
 def test_accumulation_demo_leg():

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 from conftest import gpu_available
-from helpers import check_bf16, check_f32, from_dev_bf16_bits, mfma_bound, to_dev, to_dev_bf16
+from helpers import check_gemm, from_dev_bf16_bits, reference, to_dev, to_dev_bf16
 from fp8_fine_grained_online_amd import synthetic as S
 
 pytestmark = [pytest.mark.gpu,
@@ -210,14 +210,7 @@ def gpu_rowscaled(qa, sa, qb, sb, out, rows=None):
 
 
 def check_rowscaled(got, qa, sa, qb, sb, out):
-    from oracle import bf16, gemm
-    c64 = gemm.gemm_rowscaled_f64(qa, sa, qb, sb)
-    S_ = gemm.abs_sum_rowscaled(qa, sa, qb, sb)
-    T = mfma_bound(qa, sa, qb, sb, row_scales=True)
-    if out == "f32":
-        return check_f32(got, c64, S_, T)
-    want = gemm.round_bf16(c64)
-    return check_bf16(got, c64, S_, T, want, bf16.ulp(want))
+    return check_gemm(got, reference(qa, sa, qb, sb, row_scales=True), out)
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 128, 128), (100, 256, 384), (300, 384, 256),
@@ -288,8 +281,7 @@ def test_dgrad_composed():
     F.fp8_gemm_blockscaled(qd, sd, qwt, swt, "f32", c=dx)
     oqd, osd = quant.quant_act_1x128(dy)
     oqwt, oswt = quant.transpose_weight_128x128(*quant.quant_weight_128x128(w))
-    c64 = gemm.gemm_blockscaled_f64(oqd, osd, oqwt, oswt)
-    check_f32(host(dx), c64, gemm.abs_sum(oqd, osd, oqwt, oswt), mfma_bound(oqd, osd, oqwt, oswt))
+    check_gemm(host(dx), reference(oqd, osd, oqwt, oswt), "f32")
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from conftest import gpu_available
-from helpers import check_bf16, check_f32, from_dev_bf16_bits, mfma_bound, to_dev, to_dev_bf16
+from helpers import check_gemm, from_dev_bf16_bits, grouped_reference, record, reference, to_dev, to_dev_bf16
 from fp8_fine_grained_online_amd import synthetic as S
 
 pytestmark = [pytest.mark.gpu,
@@ -38,29 +38,41 @@ def gpu_pipeline(a_bits, b_bits, out, rows=None):
 
 
 def oracle_rows(a_bits, b_bits, rows=None):
-    """(C64, S, T) from the oracle's own quantization of the same bytes."""
-    from oracle import gemm, quant
+    """reference() (C64, S, T, C_mfma) from the oracle's own quantization of the same bytes."""
+    from oracle import quant
     a = a_bits if rows is None else a_bits[rows]
     qa, sa = quant.quant_act_1x128(a)
     qb, sb = quant.quant_weight_128x128(b_bits)
-    return (gemm.gemm_blockscaled_f64(qa, sa, qb, sb), gemm.abs_sum(qa, sa, qb, sb),
-            mfma_bound(qa, sa, qb, sb))
+    return reference(qa, sa, qb, sb)
 
 
-def check(got, c64, S_, T, out):
-    from oracle import bf16, gemm
-    if out == "f32":
-        return check_f32(got, c64, S_, T)
-    want = gemm.round_bf16(c64)
-    return check_bf16(got, c64, S_, T, want, bf16.ulp(want))
+def check(got, ref, out):
+    return check_gemm(got, ref, out)
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_small_workload_256x256x1024(out):
     w = S.WORKLOADS["dense_256x256x1024"]
     a, b = S.dense_inputs(w)
-    c64, S_, T = oracle_rows(a, b)
-    check(gpu_pipeline(a, b, out), c64, S_, T, out)
+    record(w.name, out, check(gpu_pipeline(a, b, out), oracle_rows(a, b), out))
+
+
+def test_strict_rule_rejects_a_perturbed_scale():
+    """The kernel's FP32 output on the 256x256x1024 workload against a
+    reference whose scale of one weight block and K group is off by 1e-4
+    relative (planted in the oracle's inputs, on the CPU): rejected. The same
+    output passes against the true scales."""
+    from oracle import quant
+    w = S.WORKLOADS["dense_256x256x1024"]
+    a, b = S.dense_inputs(w)
+    got = gpu_pipeline(a, b, "f32")
+    qa, sa = quant.quant_act_1x128(a)
+    qb, sb = quant.quant_weight_128x128(b)
+    check(got, reference(qa, sa, qb, sb), "f32")
+    sb_bad = sb.astype(np.float64)
+    sb_bad[1, 3] *= 1 + 1e-4
+    with pytest.raises(AssertionError, match="matrix-core model"):
+        check(got, reference(qa, sa, qb, sb_bad), "f32")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 128), (100, 256, 384), (300, 384, 256),
@@ -69,8 +81,7 @@ def test_small_workload_256x256x1024(out):
 def test_ragged_shapes(M, N, K, out):
     a = S.activations(M, K, S.rng_for(800 + M, N))
     b = S.weights(N, K, S.rng_for(800 + M, N + 1))
-    c64, S_, T = oracle_rows(a, b)
-    check(gpu_pipeline(a, b, out), c64, S_, T, out)
+    check(gpu_pipeline(a, b, out), oracle_rows(a, b), out)
 
 
 @pytest.mark.parametrize("M", [2000, 1900])
@@ -86,8 +97,7 @@ def test_big_tile_path_ragged_m_and_n(M):
                                      S.rng_for(860, 2).integers(0, M, 20)]))
     for out in ["f32", "bf16"]:
         got = gpu_pipeline(a, b, out, rows=rows)
-        c64, S_, T = oracle_rows(a, b, rows)
-        check(got, c64, S_, T, out)
+        check(got, oracle_rows(a, b, rows), out)
 
 
 def test_one_hot_layout():
@@ -152,12 +162,13 @@ FULL = ["dense_4096x4096x4096", "proj_8192x7168x2048", "proj_8192x2048x7168", "s
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_rows(name):
+    """bf16 (the workload's output) and fp32 on sampled rows, every column."""
     w = S.WORKLOADS[name]
     a, b = S.dense_inputs(w)
     rows = np.unique(np.concatenate([[0, w.M - 1], S.rng_for(830, w.wid).integers(0, w.M, 14)]))
-    got = gpu_pipeline(a, b, "bf16", rows=rows)
-    c64, S_, T = oracle_rows(a, b, rows)
-    check(got, c64, S_, T, "bf16")
+    ref = oracle_rows(a, b, rows)
+    for out in ["bf16", "f32"]:
+        record(name, out, check(gpu_pipeline(a, b, out, rows=rows), ref, out))
 
 
 # ---------------------------------------------------------------- grouped
@@ -189,14 +200,7 @@ def grouped_case(counts, N, K, seed, out):
     qa, sa = quant.quant_act_1x128(a)
     qs = [quant.quant_weight_128x128(b[e]) for e in range(G)]
     qb, sb = np.stack([x[0] for x in qs]), np.stack([x[1] for x in qs])
-    c64 = gemm.gemm_grouped_f64(qa, sa, qb, sb, off)
-    S_ = gemm.abs_sum_grouped(qa, sa, qb, sb, off)
-    T = np.zeros_like(S_)
-    for e in range(G):
-        r = slice(off[e], off[e + 1])
-        if off[e + 1] > off[e]:
-            T[r] = mfma_bound(qa[r], sa[r], qb[e], sb[e])
-    check(got, c64, S_, T, out)
+    check(got, grouped_reference(qa, sa, qb, sb, off), out)
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
@@ -218,16 +222,17 @@ def test_grouped_full_size_sampled_experts():
     w = S.WORKLOADS["moe_g32_65536x4096x7168"]
     a, b, counts, off = S.grouped_inputs(w)
     c = gpu_grouped(a, b, off, "bf16")
+    c32 = gpu_grouped(a, b, off, "f32")
     rng = S.rng_for(850, 0)
     for e in [0, int(rng.integers(1, w.G - 1)), w.G - 1]:
         r0, r1 = int(off[e]), int(off[e + 1])
         rows = np.unique(np.concatenate([[r0, r1 - 1], rng.integers(r0, r1, 6)]))
-        got = from_dev_bf16_bits(c[torch.as_tensor(rows, device="cuda")])
+        idx = torch.as_tensor(rows, device="cuda")
         qa, sa = quant.quant_act_1x128(a[rows])
         qb, sb = quant.quant_weight_128x128(b[e])
-        c64 = gemm.gemm_blockscaled_f64(qa, sa, qb, sb)
-        S_ = gemm.abs_sum(qa, sa, qb, sb)
-        check(got, c64, S_, mfma_bound(qa, sa, qb, sb), "bf16")
+        ref = reference(qa, sa, qb, sb)
+        record(w.name, "bf16", check(from_dev_bf16_bits(c[idx]), ref, "bf16"))
+        record(w.name, "f32", check(c32[idx].cpu().numpy(), ref, "f32"))
         # padding rows of this expert are exactly zero
         if counts[e] < r1 - r0:
             pad = c[r0 + int(counts[e]):r1].float()
@@ -257,8 +262,7 @@ def test_split_k_workspace_path(M, N, K, out):
     assert (F.lib().fp8_gemm_blockscaled_ws_bytes(M, N, K) > 0) == (K >= 2048)
     a = S.activations(M, K, S.rng_for(870 + M, N))
     b = S.weights(N, K, S.rng_for(870 + M, N + 1))
-    c64, S_, T = oracle_rows(a, b)
-    check(gpu_pipeline_ws(a, b, out), c64, S_, T, out)
+    check(gpu_pipeline_ws(a, b, out), oracle_rows(a, b), out)
 
 
 def test_split_k_workspace_reuse_across_calls_and_shapes():
@@ -294,12 +298,7 @@ def test_split_k_full_size_64x7168x7168_sampled_columns():
     qa, sa = quant.quant_act_1x128(a)
     qb, sb = quant.quant_weight_128x128(b)
     sb_rows = np.repeat(sb, 128, axis=0)[cols]
-    c64 = gemm.gemm_rowscaled_f64(qa, sa, qb[cols], sb_rows)
-    S_ = gemm.abs_sum_rowscaled(qa, sa, qb[cols], sb_rows)
-    T = mfma_bound(qa, sa, qb[cols], sb_rows, row_scales=True)
-    from oracle import bf16
-    want = gemm.round_bf16(c64)
-    check_bf16(got[:, cols], c64, S_, T, want, bf16.ulp(want))
+    check(got[:, cols], reference(qa, sa, qb[cols], sb_rows, row_scales=True), "bf16")
 
 
 def test_calls_run_on_the_callers_stream():

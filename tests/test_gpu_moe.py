@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from conftest import gpu_available
-from helpers import check_bf16, from_dev_bf16_bits, mfma_bound, to_dev, to_dev_bf16
+from helpers import check_gemm, from_dev_bf16_bits, grouped_reference, to_dev, to_dev_bf16
 from fp8_fine_grained_online_amd import synthetic as S
 
 pytestmark = [pytest.mark.gpu,
@@ -136,14 +136,6 @@ def test_dispatch_feeds_grouped_gemm_without_host_sync():
     qw, sw = zip(*[quant.quant_weight_128x128(w[e]) for e in range(G)])
     qw, sw = np.stack(qw), np.stack(sw)
     M = int(off_o[-1])
-    c64 = gemm.gemm_grouped_f64(a_o, sa_o, qw, sw, off_o)
-    S_ = gemm.abs_sum_grouped(a_o, sa_o, qw, sw, off_o)
-    T_ = np.zeros_like(c64)
-    for e in range(G):
-        r = slice(int(off_o[e]), int(off_o[e + 1]))
-        if off_o[e + 1] > off_o[e]:
-            T_[r] = mfma_bound(a_o[r], sa_o[r], qw[e], sw[e])
     got = from_dev_bf16_bits(c)
-    want = gemm.round_bf16(c64)
-    check_bf16(got[:M], c64, S_, T_, want, bf16.ulp(want))
+    check_gemm(got[:M], grouped_reference(a_o[:M], sa_o[:M], qw, sw, off_o), "bf16")
     assert np.all(np.isnan(c[M:].float().cpu().numpy()))
