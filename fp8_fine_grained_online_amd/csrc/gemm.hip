@@ -14,10 +14,20 @@
 // Tiling. A workgroup computes a BM x BN output tile with WAVES_M x WAVES_N
 // waves; each wave owns a WM x WN sub-tile (WM = BM / WAVES_M, WN = BN /
 // WAVES_N <= 128, so a wave's columns share one weight block and one sb).
-// Per K group the workgroup stages the BM x 128 slab of A, the BN x 128 slab
-// of B and the BM A-scales of that group in LDS. The copies go straight from
-// global memory to LDS (buffer_load_dwordx4 ... lds: no VGPR round trip), into
-// one of two stages, so the loads of group g+1 run under the MFMAs of group g.
+// Per K group the workgroup stages the BM x 128 slab of A and the BN x 128
+// slab of B in LDS. The copies go straight from global memory to LDS
+// (buffer_load_dwordx4 ... lds: no VGPR round trip), into one of two stages,
+// so the loads of group g+1 run under the MFMAs of group g.
+//
+// A-scales: a row's scales of consecutive K groups are contiguous in sa
+// (M x K/128, row-major), so the tile's scales travel in chunks of
+// kScaleChunk groups: 16 contiguous bytes per thread, one copy per thread per
+// chunk, into a two-slot ring (slot layout [row][kScaleChunk]). Copying each
+// group's BM scales separately touches one 128-byte line per row and group,
+// as many line requests as the operand slabs themselves, and stalled the
+// texture addresser; the chunked copy took 4096^3 from 63.1 to 60.9 us and
+// 8192x2048x7168 from 105.9 to 102.2 us on one MI355X (same results bit
+// for bit).
 //
 // LDS layout: rows of 128 bytes; the eight 16-byte chunks of row r are stored
 // at chunk positions c ^ (r & 7), so the 16 rows read by one MFMA operand
@@ -66,6 +76,9 @@ struct GemmArgs {
   int n_tiles;  // number of real tiles (dense) / upper bound (grouped)
 };
 
+// K groups per A-scale chunk (8 groups: 32 bytes of each row's scales)
+constexpr int kScaleChunk = 8;
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kRowB = false>
 struct TileCfg {
   static constexpr int kWM = BM / WAVES_M;
@@ -75,18 +88,19 @@ struct TileCfg {
   static constexpr int kSubN = kWN / 16;
   static constexpr int kLdsA = BM * 128;  // bytes per stage
   static constexpr int kLdsB = BN * 128;
-  static constexpr int kLdsSa = BM * 4;
-  static constexpr int kLdsSb = kRowB ? BN * 4 : 0;  // row scales of B (kRowB only)
-  static constexpr int kStage = kLdsA + kLdsB + kLdsSa + kLdsSb;
-  // waves copying one 64-scale panel each: BM/64 for A, BN/64 more for B's row scales
-  static constexpr int kScaleWaves = BM / 64 + (kRowB ? BN / 64 : 0);
-  static constexpr int kLdsBytes = 2 * kStage;
+  static constexpr int kStage = kLdsA + kLdsB;
+  // scale ring: rows whose per-group scales are staged (A rows; with kRowB
+  // also B's rows), kScaleChunk groups per slot, two slots
+  static constexpr int kScaleRows = BM + (kRowB ? BN : 0);
+  static constexpr int kSlot = kScaleRows * kScaleChunk * 4;
+  static constexpr int kScaleCopies = kSlot / 16 / kThreads;  // 16-byte pieces per thread per chunk
+  static constexpr int kLdsBytes = 2 * kStage + 2 * kSlot;
   static constexpr int kLoadsA = BM * 8 / kThreads;  // 16-byte chunks per thread per group
   static constexpr int kLoadsB = BN * 8 / kThreads;
   static_assert(kWN <= 128 && 128 % kWN == 0, "a wave's columns must share one weight block");
   static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "whole wave loads");
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && kScaleWaves * 64 <= kThreads,
-                "scales: whole waves, one per thread");
+  static_assert(kSlot % (16 * kThreads) == 0 && BM * kScaleChunk * 4 % (16 * kThreads) == 0,
+                "scale chunks: whole pieces per thread, A and B rows in separate copies");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
@@ -151,19 +165,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(p.a + (int64_t)m0 * p.K, (uint32_t)rows_a * (uint32_t)p.K);
   const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(bmat + (int64_t)n0 * p.K, (uint32_t)rows_b * (uint32_t)p.K);
   const __amdgpu_buffer_rsrc_t rsrc_sa = make_rsrc(p.sa + (int64_t)m0 * G, (uint32_t)rows_a * (uint32_t)G * 4);
-  // scale panels: wave w (mod kScaleWaves) copies 64 A-scales, or with kRowB
-  // 64 row scales of B, of each group (waves past kScaleWaves repeat a copy:
-  // same bytes, same place, and no wave-dependent branch in the step)
-  const int sw = wave % Cfg::kScaleWaves;
-  const bool sb_wave = kRowB && sw >= BM / 64;
-  const int s_panel = sb_wave ? sw - BM / 64 : sw;
-  __amdgpu_buffer_rsrc_t rsrc_s = rsrc_sa;
-  if constexpr (kRowB) {
-    if (sb_wave)
-      rsrc_s = make_rsrc(p.sb + (int64_t)n0 * G, (uint32_t)rows_b * (uint32_t)G * 4);
-  }
-  const int s_lds = Cfg::kLdsA + Cfg::kLdsB + (sb_wave ? Cfg::kLdsSa : 0) + s_panel * 64 * 4;
-  const uint32_t offs = (uint32_t)(s_panel * 64 + lane) * (uint32_t)G * 4;
+  __amdgpu_buffer_rsrc_t rsrc_sbr = rsrc_sa;  // kRowB: B's row scales over the tile's valid columns
+  if constexpr (kRowB)
+    rsrc_sbr = make_rsrc(p.sb + (int64_t)n0 * G, (uint32_t)rows_b * (uint32_t)G * 4);
+  // Scale chunk piece q * kThreads + tid: row (piece / 2) of the ring, bytes
+  // 16 (piece % 2) .. + 16 of that row's kScaleChunk scales. The whole offset
+  // is per lane, where the buffer range check covers it: rows past the valid
+  // ones and groups past G read as zeros.
+  const uint32_t sc_row_off = (uint32_t)(tid >> 1) * (uint32_t)G * 4 + (uint32_t)(tid & 1) * 16;
+  static_assert(Cfg::kThreads == 2 * BM && (!kRowB || BN == BM), "two threads per ring row and copy");
+  uint8_t* const ring = lds + 2 * Cfg::kStage;
+  // chunk `chunk` of the tile's scales into its ring slot
+  auto issue_scales = [&](int chunk, uint8_t* __restrict__ slot) {
+    const uint32_t off = sc_row_off + (uint32_t)chunk * (kScaleChunk * 4);
+#pragma unroll
+    for (int q = 0; q < Cfg::kScaleCopies; ++q) {
+      // pieces of A rows first (q * kThreads < 2 BM), then B rows (kRowB)
+      const bool a_rows = q * Cfg::kThreads < 2 * BM;
+      const uint32_t row_base = a_rows ? (uint32_t)(q * Cfg::kThreads / 2) : (uint32_t)(q * Cfg::kThreads / 2 - BM);
+      load_lds(a_rows ? rsrc_sa : rsrc_sbr, slot + (q * Cfg::kThreads + wave * 64) * 16, 16,
+               off + row_base * (uint32_t)G * 4, 0);
+    }
+  };
   // Slot q * kThreads + tid has row q * (kThreads / 8) + tid / 8 and stored
   // chunk tid % 8, so copy q's per-lane offset is offa + q * row_step. The row
   // part must stay in the per-lane offset: the buffer range check covers the
@@ -176,17 +199,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const uint32_t row_step = (uint32_t)(Cfg::kThreads / 8) * (uint32_t)p.K;
 
   // Copy number q (0 .. kCopies-1) of this thread's share of group g into `stage`.
-  constexpr int kCopies = Cfg::kLoadsA + Cfg::kLoadsB + 1;
+  constexpr int kCopies = Cfg::kLoadsA + Cfg::kLoadsB;
   auto issue_copy = [&](int q, int g, uint8_t* __restrict__ stage) {
     if (q < Cfg::kLoadsA) {
       load_lds(rsrc_a, stage + (q * Cfg::kThreads + wave * 64) * 16, 16, offa + q * row_step,
                g * kGroup);
-    } else if (q < Cfg::kLoadsA + Cfg::kLoadsB) {
+    } else {
       const int i = q - Cfg::kLoadsA;
       load_lds(rsrc_b, stage + Cfg::kLdsA + (i * Cfg::kThreads + wave * 64) * 16, 16,
                offb + i * row_step, g * kGroup);
-    } else {
-      load_lds(rsrc_s, stage + s_lds, 4, offs, g * 4);
     }
   };
   auto issue_loads = [&](int g, uint8_t* __restrict__ stage) {
@@ -245,20 +266,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
 #pragma unroll
     for (int r = 0; r < 4; ++r) c[r] = __builtin_fmaf(part[r], kRowB ? sbr[r] * sa1 : sc1, c[r]);
   };
+  // scol: the ring column of this group's scales (row r at scol[r * kScaleChunk]);
+  // chunk >= 0: copy that scale chunk into `nslot` during this step.
   auto step = [&](const uint8_t* __restrict__ stage, uint8_t* __restrict__ nxt, int g_next,
-                  float sbv) {
+                  float sbv, const float* __restrict__ scol, int chunk, uint8_t* __restrict__ nslot) {
     const uint8_t* sA = stage;
     const uint8_t* sB = stage + Cfg::kLdsA;
-    const float* sSa = (const float*)(stage + Cfg::kLdsA + Cfg::kLdsB) + wm * WM + lr;
+    const float* sSa = scol + (wm * WM + lr) * kScaleChunk;
     v8i bf[SUBN];
 #pragma unroll
     for (int j = 0; j < SUBN; ++j) bf[j] = load_frag(sB + (wn * WN + j * 16) * 128);
     // kRowB: the row scales of the lane's four columns in each 16-column block
     v4f sbq[kRowB ? SUBN : 1];
     if constexpr (kRowB) {
-      const float* sSb = (const float*)(stage + Cfg::kLdsA + Cfg::kLdsB + Cfg::kLdsSa) + wn * WN + 4 * lk;
+      const float* sSb = scol + (BM + wn * WN + 4 * lk) * kScaleChunk;
 #pragma unroll
-      for (int j = 0; j < SUBN; ++j) sbq[j] = *(const v4f*)(sSb + j * 16);
+      for (int j = 0; j < SUBN; ++j)
+        sbq[j] = v4f{sSb[(j * 16) * kScaleChunk], sSb[(j * 16 + 1) * kScaleChunk],
+                     sSb[(j * 16 + 2) * kScaleChunk], sSb[(j * 16 + 3) * kScaleChunk]};
     }
     // A fragment and A-scale of 16-row block i+1 are read while block i multiplies
     v8i af = load_frag(sA + wm * WM * 128);
@@ -273,11 +298,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
       const int i = t / SUBN, j = t % SUBN;
       if (t >= kCopyOff && (t - kCopyOff) % kCopyEvery == 0 && (t - kCopyOff) / kCopyEvery < kCopies)
         issue_copy((t - kCopyOff) / kCopyEvery, g_next, nxt);
+      if (t == 1 && chunk >= 0) issue_scales(chunk, nslot);
       if (j == 0) {
         sc = sav * sbv;
         if (i + 1 < SUBM) {
           af_next = load_frag(sA + (wm * WM + (i + 1) * 16) * 128);
-          sav_next = sSa[(i + 1) * 16];
+          sav_next = sSa[(i + 1) * 16 * kScaleChunk];
         }
       }
       const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -311,22 +337,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const bool idle = wm * WM >= rows_a;
 
   // ---- main loop: group g computes from stage g % 2 while g+1 streams into the other ----
+  // Scale chunk c (groups kScaleChunk c ..) lives in ring slot c % 2. Chunk
+  // c + 1 is copied during the first step of chunk c, into the slot chunk
+  // c - 1 used: every wave finished chunk c - 1's last group before the
+  // barrier that ends it.
   float sbv = 0.0f;
   if (G > 0) {
     if constexpr (!kRowB) sbv = gsb[0];
     issue_loads(0, lds);
+    issue_scales(0, ring);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   for (int g = 0; g < G; ++g) {
     uint8_t* cur = lds + (g & 1) * Cfg::kStage;
     uint8_t* nxt = lds + ((g + 1) & 1) * Cfg::kStage;
+    const int c = g / kScaleChunk;
+    const int next_chunk = (g % kScaleChunk == 0 && (c + 1) * kScaleChunk < G) ? c + 1 : -1;
+    uint8_t* nslot = ring + ((c + 1) & 1) * Cfg::kSlot;
+    const float* scol = (const float*)(ring + (c & 1) * Cfg::kSlot) + g % kScaleChunk;
     const float sbv_next = (!kRowB && g + 1 < G) ? gsb[g + 1] : 0.0f;
     // the last group re-copies itself into the idle stage (never read): no branch in the step
-    if (idle)
+    if (idle) {
       issue_loads(min(g + 1, G - 1), nxt);
-    else
-      step(cur, nxt, min(g + 1, G - 1), sbv);
+      if (next_chunk >= 0) issue_scales(next_chunk, nslot);
+    } else {
+      step(cur, nxt, min(g + 1, G - 1), sbv, scol, next_chunk, nslot);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this thread's copies have landed
     __syncthreads();                     // ... and everyone's; `cur` is free again
     sbv = sbv_next;

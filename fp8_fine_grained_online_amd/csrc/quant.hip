@@ -71,54 +71,60 @@ __global__ __launch_bounds__(kActThreads) void quant_act_1x128_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 128x128 weight quantization: one workgroup per block, the whole block
-// (32 KB of bf16) held in registers: 256 threads x 8 chunks of 16 bytes.
-// Thread t owns chunk column t % 16 of rows t / 16 + 16 i, i = 0..7.
+// 128x128 weight quantization: one workgroup per strip of kBk blocks side by
+// side along K (128 rows x 128 kBk columns), held in registers: kThreads
+// threads x kChunks chunks of 16 bytes. The kCols = 16 kBk threads of a row
+// read 256 kBk contiguous bytes of it (wider strips: longer contiguous runs
+// per row). Thread t owns chunk column t % kCols (block (t % kCols) / 16 of
+// the strip) of rows t / kCols + kRowStep i, i = 0 .. kChunks - 1.
+// A block's amax: each 16-lane DPP row holds 16 chunks of one block row
+// segment; the DPP rows' maxima meet in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kWThreads = 256;
-
-template <bool kNt>
-__global__ __launch_bounds__(kWThreads) void quant_weight_128x128_kernel(
+template <bool kNt, int kBk, int kThreads>
+__global__ __launch_bounds__(kThreads) void quant_weight_128x128_kernel(
     const uint4* __restrict__ w, uint2* __restrict__ q, float* __restrict__ sb, int64_t K,
     int nblk_k) {
-  __shared__ uint32_t wave_max[kWThreads / 64];
-  const int bk = blockIdx.x;
+  static_assert(kBk == 1 || kBk == 2 || kBk == 4, "a DPP row belongs to one block");
+  constexpr int kCols = 16 * kBk;              // chunk columns of the strip
+  constexpr int kRowStep = kThreads / kCols;   // rows between a thread's chunks
+  constexpr int kChunks = 128 / kRowStep;      // chunks per thread
+  static_assert(kThreads % kCols == 0 && 128 % kRowStep == 0, "whole rows per pass");
+  __shared__ uint32_t group_max[kThreads / 16];
+  const int bk0 = blockIdx.x * kBk;
   const int64_t bn = blockIdx.y;
   const int t = threadIdx.x;
   const int64_t chunks_per_row = K / 8;
-  const int64_t c0 = (bn * kGroup + (t >> 4)) * chunks_per_row + (int64_t)bk * 16 + (t & 15);
-  uint4 v[8];
+  const int64_t c0 = (bn * kGroup + t / kCols) * chunks_per_row + (int64_t)bk0 * 16 + t % kCols;
+  uint4 v[kChunks];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = load_nt(w + c0 + (int64_t)i * 16 * chunks_per_row);
+  for (int i = 0; i < kChunks; ++i) v[i] = load_nt(w + c0 + (int64_t)i * kRowStep * chunks_per_row);
 
   float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v[i].x)), fabsf(bf16_hi(v[i].x))),
-                       fmaxf(fabsf(bf16_lo(v[i].y)), fabsf(bf16_hi(v[i].y)))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v[i].z)), fabsf(bf16_hi(v[i].z))),
-                       fmaxf(fabsf(bf16_lo(v[i].w)), fabsf(bf16_hi(v[i].w)))));
-  }
-  uint32_t mb = row16_max_u32(__float_as_uint(m));
-  mb = umax(umax(__builtin_amdgcn_readlane(mb, 0), __builtin_amdgcn_readlane(mb, 16)),
-            umax(__builtin_amdgcn_readlane(mb, 32), __builtin_amdgcn_readlane(mb, 48)));
-  if ((t & 63) == 0) wave_max[t >> 6] = mb;
+  for (int i = 0; i < kChunks; ++i) m = fmaxf(m, absmax8(v[i]));
+  // 16-lane group g = t / 16 covers block g % kBk of the strip
+  const uint32_t mb_row = row16_max_u32(__float_as_uint(m));
+  if ((t & 15) == 0) group_max[t >> 4] = mb_row;
   __syncthreads();
-  mb = umax(umax(wave_max[0], wave_max[1]), umax(wave_max[2], wave_max[3]));
+  const int blk = (t >> 4) % kBk;
+  uint32_t mb = 0;
+#pragma unroll
+  for (int g = 0; g < kThreads / 16; g += kBk) mb = umax(mb, group_max[g + blk]);
   const float amax = __uint_as_float(mb);
   const float s = tile_scale(amax);
   const TileDivisor d = make_divisor(s, amax);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kChunks; ++i) {
     const uint2 o = quant8(v[i], d);
+    const int64_t c = c0 + (int64_t)i * kRowStep * chunks_per_row;
     if constexpr (kNt) {
-      __builtin_nontemporal_store(o.x, &q[c0 + (int64_t)i * 16 * chunks_per_row].x);
-      __builtin_nontemporal_store(o.y, &q[c0 + (int64_t)i * 16 * chunks_per_row].y);
+      __builtin_nontemporal_store(o.x, &q[c].x);
+      __builtin_nontemporal_store(o.y, &q[c].y);
     } else {
-      q[c0 + (int64_t)i * 16 * chunks_per_row] = o;
+      q[c] = o;
     }
   }
-  if (t == 0) sb[bn * nblk_k + bk] = s;
+  if (t < kCols && (t & 15) == 0) sb[bn * nblk_k + bk0 + blk] = s;
 }
 
 // Codes beyond the 256 MB Infinity Cache cannot stay cached for the kernel
@@ -140,16 +146,37 @@ hipError_t launch_quant_act_1x128(const void* x, int64_t M, int64_t K, uint8_t* 
   return hipGetLastError();
 }
 
+// 8 chunks (128 bytes of bf16) per thread whatever the strip width
+template <int kBk>
+static void launch_weight(const void* w, int64_t N, int64_t K, uint8_t* q, float* sb,
+                          hipStream_t stream) {
+  constexpr int kThreads = 256 * kBk;
+  const int nblk_k = (int)(K / kGroup);
+  const dim3 grid((unsigned)(nblk_k / kBk), (unsigned)(N / kGroup));
+  if (N * K > kCachedCodesMax)
+    hipLaunchKernelGGL((quant_weight_128x128_kernel<true, kBk, kThreads>), grid, dim3(kThreads), 0,
+                       stream, (const uint4*)w, (uint2*)q, sb, K, nblk_k);
+  else
+    hipLaunchKernelGGL((quant_weight_128x128_kernel<false, kBk, kThreads>), grid, dim3(kThreads), 0,
+                       stream, (const uint4*)w, (uint2*)q, sb, K, nblk_k);
+}
+
+// Blocks per workgroup strip along K: 2 where K / 128 is even, else 1.
+// Measured on MI355X, 131072 x 7168 (32 experts' weights, non-temporal
+// codes): 1 block per workgroup 5.71-5.78 TB/s, 2 blocks x 512 threads
+// 6.26 TB/s, 4 blocks x 1024 threads 4.89 TB/s (4 x 512: 5.51); codes and
+// scales identical across all of them.
+constexpr int kWeightStrip = 2;
+
 hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* q, float* sb,
                                        hipStream_t stream) {
-  const int nblk_k = (int)(K / kGroup);
-  const int nblk_n = (int)(N / kGroup);
-  if (N * K > kCachedCodesMax)
-    hipLaunchKernelGGL(quant_weight_128x128_kernel<true>, dim3(nblk_k, nblk_n), dim3(kWThreads), 0, stream,
-                       (const uint4*)w, (uint2*)q, sb, K, nblk_k);
+  const int64_t nblk_k = K / kGroup;
+  if (kWeightStrip >= 4 && nblk_k % 4 == 0)
+    launch_weight<4>(w, N, K, q, sb, stream);
+  else if (kWeightStrip >= 2 && nblk_k % 2 == 0)
+    launch_weight<2>(w, N, K, q, sb, stream);
   else
-    hipLaunchKernelGGL(quant_weight_128x128_kernel<false>, dim3(nblk_k, nblk_n), dim3(kWThreads), 0, stream,
-                       (const uint4*)w, (uint2*)q, sb, K, nblk_k);
+    launch_weight<1>(w, N, K, q, sb, stream);
   return hipGetLastError();
 }
 
