@@ -12,6 +12,7 @@ FP8Q_OUT_BF16 = 1
 STATUS = {
     0: "FP8Q_OK", 1: "FP8Q_ERR_NULL", 2: "FP8Q_ERR_SHAPE", 3: "FP8Q_ERR_ALIGN",
     4: "FP8Q_ERR_DTYPE", 5: "FP8Q_ERR_LAUNCH", 6: "FP8Q_ERR_NO_DEVICE", 7: "FP8Q_ERR_TOO_LARGE",
+    8: "FP8Q_ERR_SCRATCH",
 }
 
 _lib = None
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_gemm_blockscaled_bf16a.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, vp, vp]
         L.fp8_gemm_blockscaled_ws.restype = i32
         L.fp8_gemm_blockscaled_ws.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp]
+        L.fp8_gemm_blockscaled_noalloc.restype = i32
+        L.fp8_gemm_blockscaled_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
         L.fp8_gemm_blockscaled_ws_bytes.restype = i64
         L.fp8_gemm_blockscaled_ws_bytes.argtypes = [i64, i64, i64]
         L.fp8_gemm_grouped.restype = i32
@@ -279,6 +282,29 @@ def _grouped_shapes(a, sa, b, sb, m_offsets, M_total):
         if tuple(sb.shape) != (G, N // 128, K // 128):
             raise ValueError(f"sb must have shape {(G, N // 128, K // 128)}, got {tuple(sb.shape)}")
     return G, N, K, M
+
+
+def fp8_gemm_blockscaled_noalloc(a, sa, b, sb, out_dtype="bf16", c=None, stream=None):
+    """fp8_gemm_blockscaled_ws with the split-K partials in the library's
+    static per-GPU scratch (no workspace; pass c to allocate nothing at all)."""
+    torch = _torch()
+    code, tdt = _out_dtype(out_dtype)
+    pa = _dev(a, "a", torch.uint8, 2)
+    psa = _dev(sa, "sa", torch.float32, 2)
+    pb = _dev(b, "b", torch.uint8, 2)
+    psb = _dev(sb, "sb", torch.float32, 2)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if K % 128 == 0 and N % 128 == 0:
+        if tuple(sa.shape) != (M, K // 128) or tuple(sb.shape) != (N // 128, K // 128):
+            raise ValueError("scale shapes must be (M, K/128) and (N/128, K/128)")
+    c = _out(c, "c", (M, N), tdt, a.device)
+    _check("fp8_gemm_blockscaled_noalloc",
+           lib().fp8_gemm_blockscaled_noalloc(pa, psa, pb, psb, c.data_ptr(), code, M, N, K,
+                                              _stream(stream)))
+    return c
 
 
 def fp8_gemm_grouped(a, sa, b, sb, m_offsets, out_dtype="bf16", c=None, M_total=None, stream=None):

@@ -28,6 +28,10 @@ hipError_t launch_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const u
 hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b,
                                  const float* sb_rows, void* c, bool bf16_out, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream);
+int64_t static_scratch_bytes();
+hipError_t launch_gemm_blockscaled_static(const uint8_t* a, const float* sa, const uint8_t* b,
+                                          const float* sb, void* c, bool bf16_out, int64_t M,
+                                          int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_gemm_quant_a(const void* a, const uint8_t* b, const float* sb, void* c,
                                bool bf16_out, int64_t M, int64_t N, int64_t K, uint8_t* qa,
                                float* sa, hipStream_t stream);
@@ -132,6 +136,7 @@ const char* fp8q_status_string(int status) {
     case FP8Q_ERR_LAUNCH: return "kernel launch failed";
     case FP8Q_ERR_NO_DEVICE: return "no gfx950 device is current";
     case FP8Q_ERR_TOO_LARGE: return "size exceeds the kernels' 32-bit indexing";
+    case FP8Q_ERR_SCRATCH: return "the split-K partials exceed the library's static scratch (8 MiB)";
     default: return "unknown status";
   }
 }
@@ -222,6 +227,18 @@ int fp8_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const uint8_t* b,
   return launched(fp8q::launch_gemm_blockscaled_ws(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16, M, N,
                                                    K, need > 0 ? (float*)workspace : nullptr,
                                                    (hipStream_t)stream));
+}
+
+int fp8_gemm_blockscaled_noalloc(const uint8_t* a, const float* sa, const uint8_t* b,
+                                 const float* sb, void* c, int out_dtype, int64_t M, int64_t N,
+                                 int64_t K, void* stream) {
+  int s = check_gemm_common(a, sa, b, sb, c, out_dtype, M, N, K);
+  if (s == -1) return FP8Q_OK;
+  if (s) return s;
+  if (fp8q::splitk_workspace_bytes(M, N, K) > fp8q::static_scratch_bytes()) return FP8Q_ERR_SCRATCH;
+  if ((s = check_device())) return s;
+  return launched(fp8q::launch_gemm_blockscaled_static(a, sa, b, sb, c, out_dtype == FP8Q_OUT_BF16,
+                                                       M, N, K, (hipStream_t)stream));
 }
 
 int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,

@@ -57,6 +57,8 @@
 // Tile order is XCD-aware: the hardware hands workgroup ids to the 8 XCDs
 // round-robin, so ids are remapped such that each XCD works on a contiguous
 // run of tiles (neighbouring tiles share A rows / B columns in its L2).
+#include <atomic>
+
 #include "common.hpp"
 #include "tiles.hpp"
 
@@ -856,6 +858,55 @@ hipError_t launch_gemm_blockscaled_ws(const uint8_t* a, const float* sa, const u
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<false>, grid, dim3(256), 0, stream, ws, c, n4, M * N, S);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Split-K partials in library-owned device memory, for callers that cannot
+// allocate: a file-scope array, one copy per GPU the library runs on, held
+// until the process ends. Host code never passes the array's name to a
+// kernel (in host code it is only a stand-in for the symbol): the device
+// address of each GPU's copy is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.
+// ---------------------------------------------------------------------------
+constexpr int64_t kStaticScratchBytes = int64_t(8) << 20;
+static __device__ __align__(256) float scratch[kStaticScratchBytes / 4];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<float*> g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+int64_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+// The current device's copy of `scratch`; resolved on the first call per device.
+static hipError_t scratch_ptr(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  float* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr = (float*)q;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);  // same value from any racing thread
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+// fp8_gemm_blockscaled_ws with the partials in `scratch` (the caller has
+// checked that splitk_workspace_bytes(M, N, K) <= kStaticScratchBytes).
+hipError_t launch_gemm_blockscaled_static(const uint8_t* a, const float* sa, const uint8_t* b,
+                                          const float* sb, void* c, bool bf16_out, int64_t M,
+                                          int64_t N, int64_t K, hipStream_t stream) {
+  float* ws = nullptr;
+  if (splitk_workspace_bytes(M, N, K) > 0) {
+    const hipError_t e = scratch_ptr(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return launch_gemm_blockscaled_ws(a, sa, b, sb, c, bf16_out, M, N, K, ws, stream);
 }
 
 hipError_t launch_gemm_rowscaled(const uint8_t* a, const float* sa, const uint8_t* b,

@@ -65,7 +65,8 @@ typedef enum {
   FP8Q_ERR_DTYPE = 4,     /* out_dtype not one of fp8q_out_dtype */
   FP8Q_ERR_LAUNCH = 5,    /* the HIP runtime refused a launch */
   FP8Q_ERR_NO_DEVICE = 6, /* no usable gfx950 device */
-  FP8Q_ERR_TOO_LARGE = 7  /* a size overflows the kernels' 32-bit tile indexing */
+  FP8Q_ERR_TOO_LARGE = 7, /* a size overflows the kernels' 32-bit tile indexing */
+  FP8Q_ERR_SCRATCH = 8    /* fp8_gemm_blockscaled_noalloc: the partials exceed its static scratch */
 } fp8q_status;
 
 typedef enum { FP8Q_OUT_F32 = 0, FP8Q_OUT_BF16 = 1 } fp8q_out_dtype;
@@ -201,6 +202,29 @@ FP8Q_API int fp8_gemm_blockscaled_bf16a(const void* a_bf16, const uint8_t* b, co
 
 /* Workspace bytes fp8_gemm_blockscaled_ws needs for this shape (0: none; -1: invalid). */
 FP8Q_API int64_t fp8_gemm_blockscaled_ws_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * fp8_gemm_blockscaled_ws without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The split-K partials go to an 8 MiB
+ * array the library keeps in device memory, one per GPU it runs on, held
+ * until the process ends. Same kernels, same results bit for bit as
+ * fp8_gemm_blockscaled_ws; arguments as for fp8_gemm_blockscaled.
+ *
+ * The partials of S splits of 64 x 128 tiles take 4 * S * M * N bytes with at
+ * most 256 split tiles, so never more than 256 * 64 * 128 * 4 = 8 MiB
+ * (64 x 7168 x 7168: 7.0 MiB); FP8Q_ERR_SCRATCH (a call needing more than
+ * 8388608 bytes) guards that bound. Shapes whose workspace size is 0 run
+ * fp8_gemm_blockscaled. The call allocates nothing (no hipMalloc, no
+ * allocating library routine); it looks up the current device's copy of the
+ * array once per device. All calls on one GPU share that GPU's copy: two
+ * calls in flight at once on one GPU (different streams) race on it. Its
+ * contents need not start at any value (every partial is written before it
+ * is read).
+ */
+FP8Q_API int fp8_gemm_blockscaled_noalloc(const uint8_t* a, const float* sa, const uint8_t* b,
+                                          const float* sb, void* c, int out_dtype, int64_t M,
+                                          int64_t N, int64_t K, void* stream);
 
 /*
  * Grouped (MoE) block-scaled FP8 GEMM: expert e owns rows

@@ -39,7 +39,7 @@ ENTRY_POINTS = ["fp8q_quant_act_1x128", "fp8q_quant_act_1x128_nt", "fp8q_quant_w
                 "fp8_gemm_grouped", "fp8q_quant_act_128x1", "fp8q_requant_1x128_to_128x1",
                 "fp8q_transpose_weight_128x128", "fp8_gemm_rowscaled", "fp8q_quant_act_1x128_128x1",
                 "fp8q_norm_quant_act_1x128", "fp8q_moe_dispatch_1x128", "fp8_gemm_blockscaled_ws",
-                "fp8_gemm_blockscaled_bf16a"]
+                "fp8_gemm_blockscaled_bf16a", "fp8_gemm_blockscaled_noalloc"]
 
 
 def test_header_declares_the_entry_points():
@@ -53,8 +53,8 @@ def test_library_exports_every_declared_symbol():
     for name in declared_symbols():
         assert hasattr(L, name), name
     assert L.fp8q_version() == 202
-    for s in range(8):
-        assert L.fp8q_status_string(s)
+    for s in range(9):
+        assert L.fp8q_status_string(s) != b"unknown status"
     assert L.fp8q_status_string(99) == b"unknown status"
 
 
@@ -251,6 +251,34 @@ def test_gemm_ws_validation():
     assert f(A, SA, B, SB, C, 1, 64, 7168, 7168, W + 4, need, None) == 3
     assert f(A, SA, B, SB, C, 1, 64, 100, 7168, W, need, None) == 2
     assert f(None, None, None, None, None, 0, 0, 128, 128, None, 0, None) == 0
+
+
+def test_noalloc_gemm_validation():
+    """Rejected before any HIP call, like fp8_gemm_blockscaled's checks."""
+    L = _lib()
+    f = L.fp8_gemm_blockscaled_noalloc
+    assert f(A, SA, B, SB, C, 1, 64, 100, 7168, None) == 2   # N % 128
+    assert f(A, SA, B, SB, C, 1, 64, 7168, 100, None) == 2   # K % 128
+    assert f(A, SA, B, SB, C, 3, 64, 7168, 7168, None) == 4  # out dtype
+    for i in range(5):
+        args = [A, SA, B, SB, C]
+        args[i] = None
+        assert f(*args, 1, 64, 7168, 7168, None) == 1, i
+    assert f(A + 8, SA, B, SB, C, 1, 64, 7168, 7168, None) == 3
+    assert f(A, SA, B, SB, C, 1, 64, 7168, (1 << 23) + 128, None) == 7
+    assert f(None, None, None, None, None, 1, 0, 7168, 7168, None) == 0  # M = 0: no-op
+
+
+def test_noalloc_partials_never_exceed_the_static_scratch():
+    """The split-K partials of every shape fit the library's 8 MiB: S splits
+    of at most 256 / tiles, 64 x 128 tiles, 4 bytes per output per split."""
+    L = _lib()
+    worst = 0
+    for M in [1, 16, 63, 64, 65, 96, 127, 128, 129, 192, 255, 256, 300, 511, 512]:
+        for N in [128, 256, 1024, 2048, 4096, 7168, 8192, 16384, 32768]:
+            for K in [2048, 4096, 7168, 16384]:
+                worst = max(worst, L.fp8_gemm_blockscaled_ws_bytes(M, N, K))
+    assert 0 < worst <= 8 << 20
 
 
 def test_quant_on_load_gemm_validation():
