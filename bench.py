@@ -591,6 +591,11 @@ def main():
     # the clock takes a few hundred microseconds of load to settle: the default
     # warms up long enough for the short steps too
     ap.add_argument("--warmup", type=int, default=200)
+    # untimed steps for this many seconds before the W warm-up steps: the
+    # shader clock needs tens of milliseconds of load to ramp, and a handful
+    # of warm-up steps (e.g. --warmup 5) leaves the timed steps on a cold
+    # clock (4096^3 GEMM measured 88 us cold against 61-66 us settled)
+    ap.add_argument("--settle", type=float, default=0.3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-grouped", action="store_true",
                     help="skip the grouped MoE GEMM line that the default workload also reports")
@@ -668,6 +673,13 @@ def main():
         if s:
             raise RuntimeError(f"launch failed with status {s}")
 
+    settle_end = time.perf_counter() + max(0.0, args.settle)
+    settle_steps = 0
+    while time.perf_counter() < settle_end:
+        for _ in range(8):
+            step()
+        settle_steps += 8
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -750,7 +762,8 @@ def main():
         "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": dict(plan["config"], buffer_copies=n_copies,
-                       buffer_MB_per_copy=round(resident / 1e6, 1)),
+                       buffer_MB_per_copy=round(resident / 1e6, 1),
+                       settle_s=args.settle, settle_steps=settle_steps),
         "roofline": roofline,
         "kernels_ms": {n: round(v, 5) for n, v in kms.items()},
         "kernels_ms_p10_p50_p90": kpct,
@@ -773,7 +786,7 @@ def main():
         del copies, plan
         out["grouped_moe"] = grouped_moe_line(args, F, S, L, dev, sp, up_bf16,
                                               steps=max(5, min(args.steps, 50)),
-                                              warmup=max(3, min(args.warmup, 20)))
+                                              warmup=20)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_fn()
         if accum_fn:
