@@ -76,6 +76,8 @@ struct GemmArgs {
   int K;
   int G;        // experts (grouped); 1 for dense
   int n_tiles;  // number of real tiles (dense) / upper bound (grouped)
+  int n_big;      // dense with a tail: workgroups of 256 x 256 tiles (columns [0, n_col_main))
+  int n_col_main; // dense with a tail: the remaining columns go in 256 x 128 tiles
 };
 
 // K groups per A-scale chunk (8 groups: 32 bytes of each row's scales)
@@ -107,13 +109,16 @@ struct TileCfg {
 };
 
 
+// One BM x BN output tile: `tile` numbers the tiles of the columns
+// [col_base, col_end) (dense) or of all experts (grouped); `lds` holds at
+// least TileCfg::kLdsBytes (two stages, the scale ring; the epilogue's staging).
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kBf16Out, bool kGrouped, bool kRowB>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kernel(GemmArgs p) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict__ lds, int tile,
+                                          int col_base, int col_end) {
   using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N, kRowB>;
   static_assert(!(kGrouped && kRowB), "row-scaled B is dense only");
   constexpr int WM = Cfg::kWM, WN = Cfg::kWN;
   constexpr int SUBM = Cfg::kSubM, SUBN = Cfg::kSubN;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Cfg::kLdsBytes];  // two stages; the epilogue's staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,10 +126,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int G = p.K / kGroup;
-  const int n_tiles_n = (p.N + BN - 1) / BN;
+  const int n_tiles_n = (col_end - col_base + BN - 1) / BN;
 
   // ---- tile -> (rows [m0, m_end), columns n0, expert) ----
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
   int m0, m_end, tile_n;
   const uint8_t* bmat = p.b;
   const float* sbmat = p.sb;
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
     m0 = tm * BM;
     m_end = min(m0 + BM, p.M);
   }
-  const int n0 = tile_n * BN;
+  const int n0 = col_base + tile_n * BN;
   const int n_last = p.N - 1;
 
   // ---- global -> LDS copies through buffer descriptors ----
@@ -440,6 +444,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   }
 }
 
+
+// The workgroup's tile. With a tail (dense, kTail), workgroups n_big.. take
+// 256 x 128 tiles of the columns [n_col_main, N): a last, partly filled wave
+// of 256 x 256 tiles becomes a full wave of tiles half as long, all in one
+// launch. Each part's tile order is XCD-aware on its own.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool kBf16Out, bool kGrouped, bool kRowB, bool kTail>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kernel(GemmArgs p) {
+  using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N, kRowB>;
+  using TailCfg = TileCfg<BM, kTail ? BN / 2 : BN, kTail ? 2 * WAVES_M : WAVES_M,
+                          kTail ? WAVES_N / 2 : WAVES_N, kRowB>;
+  static_assert(!kTail || (!kGrouped && TailCfg::kThreads == Cfg::kThreads), "tail: dense, same workgroup");
+  constexpr int kLds = (kTail && TailCfg::kLdsBytes > Cfg::kLdsBytes) ? TailCfg::kLdsBytes : Cfg::kLdsBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  if constexpr (kTail) {
+    if ((int)blockIdx.x >= p.n_big) {
+      const int n_half = (int)gridDim.x - p.n_big;
+      gemm_tile<BM, BN / 2, 2 * WAVES_M, WAVES_N / 2, kBf16Out, kGrouped, kRowB>(
+          p, lds, xcd_tile((int)blockIdx.x - p.n_big, n_half), p.n_col_main, p.N);
+    } else {
+      gemm_tile<BM, BN, WAVES_M, WAVES_N, kBf16Out, kGrouped, kRowB>(
+          p, lds, xcd_tile(blockIdx.x, p.n_big), 0, p.n_col_main);
+    }
+  } else {
+    gemm_tile<BM, BN, WAVES_M, WAVES_N, kBf16Out, kGrouped, kRowB>(
+        p, lds, xcd_tile(blockIdx.x, gridDim.x), 0, p.N);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Small-M GEMM (HBM-bound shapes such as 64 x 7168 x 7168). A workgroup owns a
@@ -782,13 +813,36 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, bool kGrouped, bool kRowB>
 static hipError_t launch_cfg(GemmArgs args, bool bf16_out, int m_tiles, hipStream_t stream) {
   using Cfg = TileCfg<BM, BN, WAVES_M, WAVES_N, kRowB>;
   args.n_tiles = m_tiles * ((args.N + BN - 1) / BN);
-  const dim3 grid((unsigned)args.n_tiles);
   const dim3 block(Cfg::kThreads);
+  // Dense tail: when the tiles fill their last wave of workgroups (one per
+  // CU) at most half, the last c tile columns, enough to hold that wave,
+  // go in BM x BN/2 tiles instead.
+  const int rem = args.n_tiles % kCus;
+  if constexpr (!kGrouped && !kRowB) {
+    if (args.n_tiles > kCus && rem > 0 && rem <= kCus / 2) {
+    const int n_tiles_n = (args.N + BN - 1) / BN;
+    const int c = (rem + m_tiles - 1) / m_tiles;  // tile columns to split
+    if (c < n_tiles_n) {
+      args.n_col_main = (n_tiles_n - c) * BN;
+      args.n_big = m_tiles * (n_tiles_n - c);
+      const int n_half = m_tiles * ((args.N - args.n_col_main) / (BN / 2));
+      const dim3 grid((unsigned)(args.n_big + n_half));
+      if (bf16_out)
+        hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, true, kGrouped, kRowB, true>),
+                           grid, block, 0, stream, args);
+      else
+        hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, false, kGrouped, kRowB, true>),
+                           grid, block, 0, stream, args);
+      return hipGetLastError();
+    }
+    }
+  }
+  const dim3 grid((unsigned)args.n_tiles);
   if (bf16_out) {
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, true, kGrouped, kRowB>),
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, true, kGrouped, kRowB, false>),
                        grid, block, 0, stream, args);
   } else {
-    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, false, kGrouped, kRowB>),
+    hipLaunchKernelGGL((gemm_blockscaled_kernel<BM, BN, WAVES_M, WAVES_N, false, kGrouped, kRowB, false>),
                        grid, block, 0, stream, args);
   }
   return hipGetLastError();

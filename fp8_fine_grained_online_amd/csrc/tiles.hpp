@@ -13,6 +13,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kXcds = 8;
+constexpr int kCus = 256;  // compute units (one large-tile workgroup each)
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in an LDS slab of
 // 128-byte rows: chunk positions are XOR row % 8, so the 16 rows read by one

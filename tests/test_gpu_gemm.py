@@ -100,6 +100,22 @@ def test_big_tile_path_ragged_m_and_n(M):
         check(got, oracle_rows(a, b, rows), out)
 
 
+@pytest.mark.parametrize("M,N,K", [(4000, 4224, 512), (4000, 4352, 384), (8192, 7168, 256)])
+def test_last_wave_split_into_half_width_tiles(M, N, K):
+    """More 256 x 256 tiles than CUs, the last wave at most half full: the
+    last tile columns run as 256 x 128 tiles in the same launch (4000 x 4224:
+    272 tiles, the last column 128 wide; 4000 x 4352: two half tiles per row
+    tile; 8192 x 7168: 896 tiles, four columns split). Sampled rows including
+    the ragged last row tile, every column, both output types."""
+    a = S.activations(M, K, S.rng_for(865, M + N), )
+    b = S.weights(N, K, S.rng_for(866, M + N))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 160, M - 1],
+                                     S.rng_for(867, N).integers(0, M, 11)]))
+    ref = oracle_rows(a, b, rows)
+    for out in ["f32", "bf16"]:
+        check(gpu_pipeline(a, b, out, rows=rows), ref, out)
+
+
 def test_one_hot_layout():
     """A single nonzero code pair lands at exactly (m0, n0) with the right scales.
 
