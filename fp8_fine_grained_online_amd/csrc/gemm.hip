@@ -82,6 +82,8 @@ struct GemmArgs {
 
 // K groups per A-scale chunk (8 groups: 32 bytes of each row's scales)
 constexpr int kScaleChunk = 8;
+// Scale-ring column swizzle of row r (see the ring's layout in gemm_tile)
+__device__ __forceinline__ int ring_swz(int r) { return (r >> 2) & 3; }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool kRowB = false>
 struct TileCfg {
@@ -97,14 +99,14 @@ struct TileCfg {
   // also B's rows), kScaleChunk groups per slot, two slots
   static constexpr int kScaleRows = BM + (kRowB ? BN : 0);
   static constexpr int kSlot = kScaleRows * kScaleChunk * 4;
-  static constexpr int kScaleCopies = kSlot / 16 / kThreads;  // 16-byte pieces per thread per chunk
+  static constexpr int kScaleCopies = kSlot / 4 / kThreads;  // scales per thread per chunk
   static constexpr int kLdsBytes = 2 * kStage + 2 * kSlot;
   static constexpr int kLoadsA = BM * 8 / kThreads;  // 16-byte chunks per thread per group
   static constexpr int kLoadsB = BN * 8 / kThreads;
   static_assert(kWN <= 128 && 128 % kWN == 0, "a wave's columns must share one weight block");
   static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "whole wave loads");
-  static_assert(kSlot % (16 * kThreads) == 0 && BM * kScaleChunk * 4 % (16 * kThreads) == 0,
-                "scale chunks: whole pieces per thread, A and B rows in separate copies");
+  static_assert(kSlot % (4 * kThreads) == 0 && BM * kScaleChunk * 4 % (4 * kThreads) == 0,
+                "scale chunks: whole copies per thread, A and B rows in separate copies");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
@@ -174,22 +176,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
   __amdgpu_buffer_rsrc_t rsrc_sbr = rsrc_sa;  // kRowB: B's row scales over the tile's valid columns
   if constexpr (kRowB)
     rsrc_sbr = make_rsrc(p.sb + (int64_t)n0 * G, (uint32_t)rows_b * (uint32_t)G * 4);
-  // Scale chunk piece q * kThreads + tid: row (piece / 2) of the ring, bytes
-  // 16 (piece % 2) .. + 16 of that row's kScaleChunk scales. The whole offset
-  // is per lane, where the buffer range check covers it: rows past the valid
-  // ones and groups past G read as zeros.
-  const uint32_t sc_row_off = (uint32_t)(tid >> 1) * (uint32_t)G * 4 + (uint32_t)(tid & 1) * 16;
-  static_assert(Cfg::kThreads == 2 * BM && (!kRowB || BN == BM), "two threads per ring row and copy");
+  // Scale ring slot: row r's kScaleChunk scales in 32 bytes, scale c at
+  // position c ^ ring_swz(r). The readers of one scale column are the 16 rows
+  // of a 16-row block (A) or rows 4 apart (kRowB's B rows); with the XOR the
+  // 16 A rows fall in 16 distinct banks instead of four rows per bank.
+  // Copy q of thread tid fills slot position q * kThreads + tid: row
+  // q * kThreads / 8 + tid / 8, position tid % 8, i.e. the scale
+  // (tid % 8) ^ ring_swz(row). The row part stays in the per-lane offset,
+  // where the buffer range check covers it: rows past the valid ones read as
+  // zeros (groups past G, never used, read the next row's first scales).
+  static_assert(Cfg::kThreads % 128 == 0, "ring_swz(row) is the same for every copy of a thread");
+  const uint32_t sc_row_off =
+      (uint32_t)(tid >> 3) * (uint32_t)G * 4 + (uint32_t)(((tid & 7) ^ ring_swz(tid >> 3)) * 4);
+  static_assert(!kRowB || BN == BM, "B rows fill whole copies");
   uint8_t* const ring = lds + 2 * Cfg::kStage;
   // chunk `chunk` of the tile's scales into its ring slot
   auto issue_scales = [&](int chunk, uint8_t* __restrict__ slot) {
     const uint32_t off = sc_row_off + (uint32_t)chunk * (kScaleChunk * 4);
 #pragma unroll
     for (int q = 0; q < Cfg::kScaleCopies; ++q) {
-      // pieces of A rows first (q * kThreads < 2 BM), then B rows (kRowB)
-      const bool a_rows = q * Cfg::kThreads < 2 * BM;
-      const uint32_t row_base = a_rows ? (uint32_t)(q * Cfg::kThreads / 2) : (uint32_t)(q * Cfg::kThreads / 2 - BM);
-      load_lds(a_rows ? rsrc_sa : rsrc_sbr, slot + (q * Cfg::kThreads + wave * 64) * 16, 16,
+      // copies of A rows first (q * kThreads < 8 BM), then B rows (kRowB)
+      const bool a_rows = q * Cfg::kThreads < 8 * BM;
+      const uint32_t row_base = a_rows ? (uint32_t)(q * Cfg::kThreads / 8) : (uint32_t)(q * Cfg::kThreads / 8 - BM);
+      load_lds(a_rows ? rsrc_sa : rsrc_sbr, slot + (q * Cfg::kThreads + wave * 64) * 4, 4,
                off + row_base * (uint32_t)G * 4, 0);
     }
   };
@@ -272,20 +281,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
 #pragma unroll
     for (int r = 0; r < 4; ++r) c[r] = __builtin_fmaf(part[r], kRowB ? sbr[r] * sa1 : sc1, c[r]);
   };
-  // scol: the ring column of this group's scales (row r at scol[r * kScaleChunk]);
-  // chunk >= 0: copy that scale chunk into `nslot` during this step.
+  // sslot, gc: the ring slot holding this group's scales and the group's
+  // column in it; chunk >= 0: copy that scale chunk into `nslot` during this step.
   auto step = [&](const uint8_t* __restrict__ stage, uint8_t* __restrict__ nxt, int g_next,
-                  float sbv, const float* __restrict__ scol, int chunk, uint8_t* __restrict__ nslot) {
+                  float sbv, const float* __restrict__ sslot, int gc, int chunk,
+                  uint8_t* __restrict__ nslot) {
     const uint8_t* sA = stage;
     const uint8_t* sB = stage + Cfg::kLdsA;
-    const float* sSa = scol + (wm * WM + lr) * kScaleChunk;
+    // the lane's A rows are wm * WM + 16 i + lr: ring_swz(row) = ring_swz(lr)
+    const float* sSa = sslot + (wm * WM + lr) * kScaleChunk + (gc ^ ring_swz(lr));
     v8i bf[SUBN];
 #pragma unroll
     for (int j = 0; j < SUBN; ++j) bf[j] = load_frag(sB + (wn * WN + j * 16) * 128);
     // kRowB: the row scales of the lane's four columns in each 16-column block
     v4f sbq[kRowB ? SUBN : 1];
     if constexpr (kRowB) {
-      const float* sSb = scol + (BM + wn * WN + 4 * lk) * kScaleChunk;
+      // rows BM + wn * WN + 16 j + 4 lk + r, r < 4: ring_swz(row) = ring_swz(4 lk)
+      const float* sSb = sslot + (BM + wn * WN + 4 * lk) * kScaleChunk + (gc ^ ring_swz(4 * lk));
 #pragma unroll
       for (int j = 0; j < SUBN; ++j)
         sbq[j] = v4f{sSb[(j * 16) * kScaleChunk], sSb[(j * 16 + 1) * kScaleChunk],
@@ -361,14 +373,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
     const int c = g / kScaleChunk;
     const int next_chunk = (g % kScaleChunk == 0 && (c + 1) * kScaleChunk < G) ? c + 1 : -1;
     uint8_t* nslot = ring + ((c + 1) & 1) * Cfg::kSlot;
-    const float* scol = (const float*)(ring + (c & 1) * Cfg::kSlot) + g % kScaleChunk;
+    const float* sslot = (const float*)(ring + (c & 1) * Cfg::kSlot);
     const float sbv_next = (!kRowB && g + 1 < G) ? gsb[g + 1] : 0.0f;
     // the last group re-copies itself into the idle stage (never read): no branch in the step
     if (idle) {
       issue_loads(min(g + 1, G - 1), nxt);
       if (next_chunk >= 0) issue_scales(next_chunk, nslot);
     } else {
-      step(cur, nxt, min(g + 1, G - 1), sbv, scol, next_chunk, nslot);
+      step(cur, nxt, min(g + 1, G - 1), sbv, sslot, g % kScaleChunk, next_chunk, nslot);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this thread's copies have landed
     __syncthreads();                     // ... and everyone's; `cur` is free again
