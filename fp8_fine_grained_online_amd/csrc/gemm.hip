@@ -827,14 +827,28 @@ __global__ __launch_bounds__(64 * kSpWaves) void gemm_splitk_kernel(GemmArgs p, 
   }
 }
 
-// C = sum over the S splits, in split order, then the output rounding
+// C = sum over the S splits, in split order, then the output rounding. The
+// partials are read kReduceBatch at a time, all loads of a batch in flight
+// together: one dependent load per split made the kernel a chain of S memory
+// latencies (about 4.5 us whatever the size).
+constexpr int kReduceBatch = 16;
+
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, void* c,
                                                             int64_t n4, int64_t MN, int S) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 consecutive outputs
   if (i >= n4) return;
-  v4f sum = *(const v4f*)(ws + 4 * i);
-  for (int s = 1; s < S; ++s) sum += *(const v4f*)(ws + (int64_t)s * MN + 4 * i);
+  const float* src = ws + 4 * i;
+  v4f sum = *(const v4f*)src;
+  for (int s0 = 1; s0 < S; s0 += kReduceBatch) {
+    v4f part[kReduceBatch];
+#pragma unroll
+    for (int u = 0; u < kReduceBatch; ++u)
+      if (s0 + u < S) part[u] = *(const v4f*)(src + (int64_t)(s0 + u) * MN);
+#pragma unroll
+    for (int u = 0; u < kReduceBatch; ++u)
+      if (s0 + u < S) sum += part[u];
+  }
   if constexpr (kBf16Out) {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     *(bf16x4*)((__bf16*)c + 4 * i) = bf16x4{(__bf16)sum[0], (__bf16)sum[1], (__bf16)sum[2], (__bf16)sum[3]};
