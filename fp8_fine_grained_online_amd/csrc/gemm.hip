@@ -28,8 +28,9 @@
 //
 // A-scales: a row's scales of consecutive K groups are contiguous in sa
 // (M x K/128, row-major), so the tile's scales travel in chunks of
-// kScaleChunk groups: 16 contiguous bytes per thread, one copy per thread per
-// chunk, into a two-slot ring (slot layout [row][kScaleChunk]). Copying each
+// kScaleChunk groups (32 bytes of each row, read by 8 neighbouring lanes)
+// into a two-slot ring, [row][kScaleChunk] with the column XOR-swizzled by
+// row (see gemm_tile). Copying each
 // group's BM scales separately touches one 128-byte line per row and group,
 // as many line requests as the operand slabs themselves, and stalled the
 // texture addresser; the chunked copy took 4096^3 from 63.1 to 60.9 us and
@@ -261,25 +262,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
 
-  // One pipeline step: compute the K group held in `stage` (sbv: its weight
-  // scale) while copying group g_next into `nxt`. The restrict-qualified
-  // stages tell the compiler (and its wait-count pass) that the LDS reads of
-  // `stage` never alias the in-flight copies into `nxt`, so those copies are
-  // not waited on until the barrier.
-  // The wave's SUBM x SUBN MFMAs run in sequence t = i * SUBN + j; the FMAs
-  // promoting MFMA t-1 are issued right after MFMA t, so each promotion waits
-  // on a result that is one MFMA old.
+  // One pipeline step: multiply the K group whose A slab is at sA (sbv: its
+  // weight scale) with the B fragments held in bf, read the next group's B
+  // fragments from sBn into bf, and copy A's slab of group ga into nxt and
+  // B's slab of group gb into cur_w. The restrict-qualified pointers tell the
+  // compiler (and its wait-count pass) that the LDS reads never alias the
+  // in-flight copies, so those copies are not waited on until the barrier.
+  // The FMAs promoting an MFMA are issued right after the next MFMA, so each
+  // promotion waits on a result that is one MFMA old.
   //
-  // The copies of the next group are spread over the MFMAs (one every
-  // kCopyEvery MFMAs, pinned by scheduling-group hints): a wave issues in
-  // order, and a burst of direct-to-LDS copies would hold back its MFMAs
-  // while the memory pipeline accepts them. They start only after the step's
-  // first kCopyOff MFMAs: until then every wave's B-fragment reads are being
-  // served, and a copy's LDS write would compete with them for LDS bandwidth.
-  // Measured on MI355X at three shapes, one copy every 2 MFMAs from MFMA 3
-  // beats one every 3 from MFMA 0 by 1-4%. The grouped GEMM, whose weights
-  // come from HBM rather than the Infinity Cache, does best with its copies
-  // one per MFMA from MFMA 3 (32-expert MoE: 2227 against 2262 us).
+  // The copies are spread over the MFMAs (one every kCopyEvery MFMAs, pinned
+  // by scheduling-group hints): a wave issues in order, and a burst of
+  // direct-to-LDS copies would hold back its MFMAs while the memory pipeline
+  // accepts them. They start after the step's first kCopyOff MFMAs. Measured
+  // on MI355X at three shapes, one copy every 2 MFMAs from MFMA 3 beat one
+  // every 3 from MFMA 0 by 1-4%, and it stayed best once the B fragments were
+  // prefetched (against offsets 0 and 3 with one copy every 1 or 2 MFMAs).
+  // The grouped GEMM, whose weights come from HBM rather than the Infinity
+  // Cache, does best with its copies one per MFMA from MFMA 3 (32-expert MoE:
+  // 2227 against 2262 us).
   constexpr int kCopyOff = 3;
   constexpr int kCopyEvery = kGrouped ? 1 : 2;
   static_assert(kCopyOff + (kCopies - 1) * kCopyEvery < SUBM * SUBN, "the copies fit in a step");
