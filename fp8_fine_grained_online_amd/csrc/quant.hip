@@ -161,19 +161,23 @@ static void launch_weight(const void* w, int64_t N, int64_t K, uint8_t* q, float
                        stream, (const uint4*)w, (uint2*)q, sb, K, nblk_k);
 }
 
-// Blocks per workgroup strip along K: 2 where K / 128 is even, else 1.
-// Measured on MI355X, 131072 x 7168 (32 experts' weights, non-temporal
-// codes): 1 block per workgroup 5.71-5.78 TB/s, 2 blocks x 512 threads
-// 6.26 TB/s, 4 blocks x 1024 threads 4.89 TB/s (4 x 512: 5.51); codes and
-// scales identical across all of them.
-constexpr int kWeightStrip = 2;
+// Blocks per workgroup strip along K: 2 for large weights where K / 128 is
+// even, else 1. Medians on MI355X (interleaved variants, three rotating
+// buffers; codes and scales identical across them), 1 / 2 / 4 blocks per
+// workgroup (256 / 512 / 1024 threads):
+//   131072 x 7168 (57344 blocks): 491 / 454 / 576 us
+//   7168 x 7168 (3136 blocks):    28.0 / 28.2 / 39.1 us
+//   4096 x 4096 (1024 blocks):    11.7 / 13.3 / 12.8 us
+//   7168 x 2048 (896 blocks):     11.4 / 12.2 / 11.9 us
+// Two-block strips keep more bytes in flight per workgroup, which pays once
+// the grid is many workgroups deep; a shallow grid does better with more,
+// smaller workgroups whose loads and stores overlap.
+constexpr int64_t kWideStripBlocks = 8192;
 
 hipError_t launch_quant_weight_128x128(const void* w, int64_t N, int64_t K, uint8_t* q, float* sb,
                                        hipStream_t stream) {
   const int64_t nblk_k = K / kGroup;
-  if (kWeightStrip >= 4 && nblk_k % 4 == 0)
-    launch_weight<4>(w, N, K, q, sb, stream);
-  else if (kWeightStrip >= 2 && nblk_k % 2 == 0)
+  if (nblk_k % 2 == 0 && (N / kGroup) * nblk_k >= kWideStripBlocks)
     launch_weight<2>(w, N, K, q, sb, stream);
   else
     launch_weight<1>(w, N, K, q, sb, stream);
