@@ -116,6 +116,23 @@ def test_last_wave_split_into_half_width_tiles(M, N, K):
         check(gpu_pipeline(a, b, out, rows=rows), ref, out)
 
 
+@pytest.mark.parametrize("M,N", [(2048, 4096), (2000, 4224)])
+@pytest.mark.parametrize("K", [128, 384, 1152])
+def test_big_tile_path_short_and_odd_k(M, N, K):
+    """The large-tile kernel's pipeline edges: one K group (the prologue's
+    copies and fragment reads only, every later copy a repeat of group 0),
+    three groups (B copied two groups ahead runs past the end at once), and
+    nine (a second, partial A-scale chunk). 2048 x 4096 is 128 tiles (no
+    tail); 2000 x 4224 is 264 tiles with ragged rows, so its last 8 tiles'
+    columns run as 256 x 128 tiles."""
+    a = S.activations(M, K, S.rng_for(868, M + K))
+    b = S.weights(N, K, S.rng_for(869, N + K))
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], S.rng_for(868, K).integers(0, M, 12)]))
+    ref = oracle_rows(a, b, rows)
+    for out in ["f32", "bf16"]:
+        check(gpu_pipeline(a, b, out, rows=rows), ref, out)
+
+
 def test_one_hot_layout():
     """A single nonzero code pair lands at exactly (m0, n0) with the right scales.
 
@@ -248,6 +265,14 @@ def grouped_case(counts, N, K, seed, out):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_grouped_small_with_empty_experts_and_padding(out):
     grouped_case([100, 0, 300, 128, 1, 0], 256, 512, 840, out)
+
+
+@pytest.mark.parametrize("K", [128, 384, 1152])
+def test_grouped_short_and_odd_k(K):
+    """The grouped kernel with one, three and nine K groups (see
+    test_big_tile_path_short_and_odd_k), experts with a 128-row remainder
+    tile, an empty expert, every output checked."""
+    grouped_case([300, 0, 700, 130], 256, K, 842 + K, "f32")
 
 
 def test_grouped_experts_taller_than_a_band():
