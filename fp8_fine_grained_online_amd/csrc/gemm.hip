@@ -90,6 +90,13 @@ struct GemmArgs {
 
 // K groups per A-scale chunk (8 groups: 32 bytes of each row's scales)
 constexpr int kScaleChunk = 8;
+// A wave's own LDS writes are complete, and neither the compiler nor the
+// hardware moves its later LDS reads (of what other lanes wrote) ahead of them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Scale-ring column swizzle of row r (see the ring's layout in gemm_tile)
 __device__ __forceinline__ int ring_swz(int r) { return (r >> 2) & 3; }
 
@@ -419,7 +426,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
     // 128 bytes with the 16-byte chunk index XOR row % 8, so the staging
     // writes of 16 rows hit distinct banks pairwise and the reads are
     // conflict-free. The loop above ends with a barrier, so no wave still
-    // reads the stages.
+    // reads the stages; each wave then reads back only what it wrote itself
+    // (a wave's LDS accesses are processed in order), so no barrier is needed
+    // between the staging writes and the reads, and a wave that finishes its
+    // MFMAs first starts storing first.
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     static_assert(WN * 2 == 128, "one 128-byte row segment per wave row");
     static_assert(WAVES_M * WAVES_N * WM * 128 <= Cfg::kLdsBytes, "staging fits in the stages");
@@ -435,7 +445,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
         *(bf16x4*)(tile + m * 128 + ((((byte >> 4) ^ (m & 7))) << 4) + (byte & 15)) = v;
       }
     }
-    __syncthreads();
+    wave_lds_sync();
     const int nw = n0 + wn * WN;  // N % 128 == 0: the wave's 64 columns are all in or all out
     if (nw < p.N) {
       const int c = lane & 7;
@@ -448,8 +458,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
       }
     }
   } else {
-    // FP32: the same staging in two passes of WM / 2 rows (a row is 256
-    // bytes, 16 chunks of 16 bytes at chunk index XOR row % 16)
+    // FP32: the same wave-local staging in two passes of WM / 2 rows (a row
+    // is 256 bytes, 16 chunks of 16 bytes at chunk index XOR row % 16); the
+    // second pass's writes follow the first pass's reads in the wave's order
     static_assert(WN * 4 == 256 && SUBM % 2 == 0, "two passes of 256-byte rows");
     static_assert(WAVES_M * WAVES_N * (WM / 2) * 256 <= Cfg::kLdsBytes, "staging fits in the stages");
     uint8_t* tile = lds + wave * ((WM / 2) * 256);
@@ -457,7 +468,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
     const int c = lane & 15;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      if (h) __syncthreads();  // the first pass's reads are done before the tile is rewritten
 #pragma unroll
       for (int i = 0; i < SUBM / 2; ++i) {
         const int m = i * 16 + lr;
@@ -465,7 +475,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
         for (int j = 0; j < SUBN; ++j)
           *(v4f*)(tile + m * 256 + (((j * 4 + lk) ^ (m & 15)) << 4)) = acc[h * (SUBM / 2) + i][j];
       }
-      __syncthreads();
+      wave_lds_sync();
       if (nw < p.N) {
 #pragma unroll
         for (int k = 0; k < WM / 8; ++k) {
