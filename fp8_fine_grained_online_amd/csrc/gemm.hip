@@ -503,13 +503,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_blockscaled_kerne
   constexpr int kLds = (kTail && TailCfg::kLdsBytes > Cfg::kLdsBytes) ? TailCfg::kLdsBytes : Cfg::kLdsBytes;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   if constexpr (kTail) {
-    if ((int)blockIdx.x >= p.n_big) {
-      const int n_half = (int)gridDim.x - p.n_big;
+    // Workgroups in three runs: h1 of the half-width tiles, all full tiles,
+    // the other half-width tiles. The CUs that start on a half-width tile run
+    // half a tile ahead of the others from then on, so each wave of tiles ends
+    // (and writes its output) in two groups half a tile apart instead of all
+    // at once. Runs start at multiples of 8 ids where the counts allow, which
+    // keeps each run's tile order XCD-aware.
+    const int id = (int)blockIdx.x;
+    const int n_half = (int)gridDim.x - p.n_big;
+    const int h1 = (n_half / 2) & ~(kXcds - 1);
+    if (id < h1) {
       gemm_tile<BM, BN / 2, 2 * WAVES_M, WAVES_N / 2, kBf16Out, kGrouped, kRowB>(
-          p, lds, xcd_tile((int)blockIdx.x - p.n_big, n_half), p.n_col_main, p.N);
-    } else {
+          p, lds, xcd_tile(id, h1), p.n_col_main, p.N);
+    } else if (id < h1 + p.n_big) {
       gemm_tile<BM, BN, WAVES_M, WAVES_N, kBf16Out, kGrouped, kRowB>(
-          p, lds, xcd_tile(blockIdx.x, p.n_big), 0, p.n_col_main);
+          p, lds, xcd_tile(id - h1, p.n_big), 0, p.n_col_main);
+    } else {
+      gemm_tile<BM, BN / 2, 2 * WAVES_M, WAVES_N / 2, kBf16Out, kGrouped, kRowB>(
+          p, lds, h1 + xcd_tile(id - h1 - p.n_big, n_half - h1), p.n_col_main, p.N);
     }
   } else {
     gemm_tile<BM, BN, WAVES_M, WAVES_N, kBf16Out, kGrouped, kRowB>(
