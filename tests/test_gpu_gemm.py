@@ -282,6 +282,17 @@ def test_grouped_experts_taller_than_a_band():
     grouped_case([4300, 0, 8400, 37], 384, 256, 841, "f32")
 
 
+def test_grouped_more_experts_than_a_wave():
+    """Each wave finds its tile's expert by scanning the experts' tile counts
+    64 experts at a time: 70 experts (two scan chunks), empty ones at both
+    ends and at the chunk boundary, a one-row expert, one taller than a
+    tile, every output checked."""
+    rng = np.random.default_rng(843)
+    counts = rng.integers(0, 300, 70)
+    counts[[0, 5, 63, 64, 69]] = [0, 1, 0, 600, 0]
+    grouped_case(counts.tolist(), 256, 256, 843, "f32")
+
+
 def test_grouped_full_size_sampled_experts():
     """G=32, N=4096, K=7168, multinomial(65536) tokens padded to 128: 3 experts checked."""
     import torch
