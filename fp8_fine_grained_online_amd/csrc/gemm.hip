@@ -275,21 +275,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
   // B's slab of group gb into cur_w. The restrict-qualified pointers tell the
   // compiler (and its wait-count pass) that the LDS reads never alias the
   // in-flight copies, so those copies are not waited on until the barrier.
-  // The FMAs promoting an MFMA are issued right after the next MFMA, so each
-  // promotion waits on a result that is one MFMA old.
   //
-  // The copies are spread over the MFMAs (one every kCopyEvery MFMAs, pinned
-  // by scheduling-group hints): a wave issues in order, and a burst of
-  // direct-to-LDS copies would hold back its MFMAs while the memory pipeline
-  // accepts them. They start after the step's first kCopyOff MFMAs. Measured
-  // on MI355X at three shapes, one copy every 2 MFMAs from MFMA 3 beat one
-  // every 3 from MFMA 0 by 1-4%, and it stayed best once the B fragments were
-  // prefetched (against offsets 0 and 3 with one copy every 1 or 2 MFMAs).
+  // The step's instruction order is fixed in the source: scheduling barriers
+  // around each MFMA keep the compiler from moving anything across it. Left
+  // free, the scheduler placed some promotion FMAs ahead of the next MFMA, on
+  // the result of the MFMA just issued: the wave then waited out that MFMA's
+  // whole latency before it could issue the next one (14 of the 128 FMAs of
+  // a step, plus 109 cycles of hazard s_nops). The FMAs promoting an MFMA are
+  // issued after the MFMA kPromoteLag places later, so each promotion reads a
+  // result that is already complete and needs no wait states (12 s_nop
+  // cycles per step). Measured on MI355X in one process, same results bit
+  // for bit: 4096^3 61.5 -> 58.4 us, 8192x2048x7168 101.0 -> 95.9 us,
+  // 8192x7168x2048 117.2 -> 114.8 us. A lag of 3 and A-fragment reads two
+  // blocks ahead measured the same or slower.
+  //
+  // The copies are spread over the MFMAs (one every kCopyEvery MFMAs): a wave
+  // issues in order, and a burst of direct-to-LDS copies would hold back its
+  // MFMAs while the memory pipeline accepts them. They start before MFMA
+  // kCopyOff. The dense GEMM does best with one copy every 2 MFMAs from MFMA 3
+  // (offsets 1, 2, 5 and spacings 1, 3 measured the same or up to 2% slower).
   // The grouped GEMM, whose weights come from HBM rather than the Infinity
-  // Cache, does best with its copies one per MFMA from MFMA 3 (32-expert MoE:
-  // 2227 against 2262 us).
-  constexpr int kCopyOff = 3;
+  // Cache, wants its copies as early as possible: one per MFMA from MFMA 0
+  // (32-expert MoE: 1860 us, against 1878, 1896 and 1921 us from MFMA 1, 2
+  // and 3).
+  constexpr int kCopyOff = kGrouped ? 0 : 3;
   constexpr int kCopyEvery = kGrouped ? 1 : 2;
+  constexpr int kPromoteLag = 2;
   static_assert(kCopyOff + (kCopies - 1) * kCopyEvery < SUBM * SUBN, "the copies fit in a step");
   // acc += part * scale: one scale for the lane's four columns (128x128 B
   // blocks: sc1 = sa * sb), or one per column (kRowB: sa * sb_row, formed
@@ -328,8 +339,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
     float sav[SUBM], scb[SUBM];
     af[0] = load_frag(sA + wm * WM * 128);
     sav[0] = sSa[0];
-    v4f part_prev;
-    int pi = 0, pj = 0;
+    // MFMA results not yet promoted: that of MFMA t sits in slot t % kPromoteLag
+    v4f pend[kPromoteLag];
+    int pend_i[kPromoteLag], pend_j[kPromoteLag];
+    auto promote_pending = [&](int slot) {
+      const int pi = pend_i[slot], pj = pend_j[slot];
+      promote(acc[pi][pj], pend[slot], scb[pi], sav[pi], sbq[kRowB ? pj : 0]);
+    };
 #pragma unroll
     for (int t = 0; t < SUBM * SUBN; ++t) {
       const int i = t < kTail0 ? t / SUBN : SUBM - 2 + (t - kTail0) % 2;
@@ -349,21 +365,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
       if (first_of_block) scb[i] = sav[i] * sbv;
       const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
           bf[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
       // block SUBM-1 is B fragment j's last use: read the next group's
       if (i == SUBM - 1) bf[j] = load_frag(sBn + (wn * WN + j * 16) * 128);
-      if (t > 0) promote(acc[pi][pj], part_prev, scb[pi], sav[pi], sbq[kRowB ? pj : 0]);
-      part_prev = part;
-      pi = i;
-      pj = j;
+      if (t >= kPromoteLag) promote_pending(t % kPromoteLag);
+      pend[t % kPromoteLag] = part;
+      pend_i[t % kPromoteLag] = i;
+      pend_j[t % kPromoteLag] = j;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    promote(acc[pi][pj], part_prev, scb[pi], sav[pi], sbq[kRowB ? pj : 0]);
-    // scheduling hint: kCopyOff MFMAs, then one copy and kCopyEvery MFMAs, repeated
-    __builtin_amdgcn_sched_group_barrier(0x008, kCopyOff, 0);  // MFMA
 #pragma unroll
-    for (int q = 0; q < kCopies; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // VMEM read (the copy)
-      __builtin_amdgcn_sched_group_barrier(0x008, kCopyEvery, 0);  // MFMA
-    }
+    for (int t = SUBM * SUBN; t < SUBM * SUBN + kPromoteLag; ++t) promote_pending(t % kPromoteLag);
   };
 
   // A wave whose 16-row blocks all lie past the tile's valid rows (the
