@@ -301,9 +301,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
   // The grouped GEMM, whose weights come from HBM rather than the Infinity
   // Cache, wants its copies as early as possible: one per MFMA from MFMA 0
   // (32-expert MoE: 1860 us, against 1878, 1896 and 1921 us from MFMA 1, 2
-  // and 3).
-  constexpr int kCopyOff = kGrouped ? 0 : 3;
-  constexpr int kCopyEvery = kGrouped ? 1 : 2;
+  // and 3). The dense tail's half-width tiles (16 MFMAs per step) do best
+  // with one copy per MFMA from MFMA 1: 8192x7168x2048 111.7 -> 109.8 us,
+  // 4000x4352x2048 47.5 -> 46.7 us (from MFMA 0, every 1 or 2, and from
+  // MFMA 2 every 2: 110.3-111.5 and 45.9-47.3 us).
+  constexpr bool kHalfWidth = !kGrouped && BN == 128;
+  constexpr int kCopyOff = kGrouped ? 0 : (kHalfWidth ? 1 : 3);
+  constexpr int kCopyEvery = kGrouped || kHalfWidth ? 1 : 2;
   constexpr int kPromoteLag = 2;
   static_assert(kCopyOff + (kCopies - 1) * kCopyEvery < SUBM * SUBN, "the copies fit in a step");
   // acc += part * scale: one scale for the lane's four columns (128x128 B
