@@ -285,9 +285,11 @@ FP8Q_API int fp8_gemm_grouped(const uint8_t* a, const float* sa, const uint8_t* 
  *                 fp8q_moe_dispatch_workspace_bytes(T, topk, G) bytes, 4-byte
  *                 aligned, owned by the caller; no contents needed on entry
  * Requires K % 128 == 0, topk >= 1, 1 <= G <= 1024. T == 0 still writes
- * m_offsets (all zero). Up to four kernels are enqueued on `stream`: count,
- * scan, rank and quantize/scatter (no count or rank kernel when T == 0, no
- * quantize/scatter kernel when K == 0).
+ * m_offsets (all zero). Up to three kernels are enqueued on `stream`: count
+ * (per-block histograms, and each slot's rank inside its block, held in
+ * row_of_slot until the last kernel), scan and quantize/scatter, which also
+ * turns the ranks into rows (only the scan when T == 0; with K == 0 the last
+ * kernel only writes the row map).
  */
 FP8Q_API int fp8q_moe_dispatch_1x128(const void* x_bf16, const int32_t* topk_ids, int64_t T,
                                      int64_t K, int64_t topk, int64_t G, uint8_t* q, float* sa,

@@ -54,13 +54,18 @@ def check_against_oracle(x, ids, G):
 
 # K up to 8192 keeps a token's codes in registers and writes each destination
 # row in one pass (8192: 8 steps, the limit); larger K stores step by step
-# The last three rows give the offsets scan several 256-slot blocks per thread
+# Rows 10-12 give the offsets scan several 256-slot blocks per thread
 # with ragged runs (305 and 625 blocks over 64 threads per expert) and, at
-# G = 600, ten experts per lane in the prefix over the experts' totals.
+# G = 600, ten experts per lane in the prefix over the experts' totals. The
+# last two give a token more choices than a wavefront has lanes: 70 (the
+# choices past 64 looked up one by one, their rows written in one batch of
+# 4 x 64 lanes) and 300 (two batches; a token's slots span two 256-slot
+# blocks).
 @pytest.mark.parametrize("T,k,G,K", [(64, 8, 32, 256), (300, 2, 7, 384), (129, 1, 1, 128),
                                      (50, 6, 256, 128), (1000, 8, 32, 1024), (257, 3, 1024, 128),
                                      (40, 4, 16, 8192), (33, 3, 8, 9216), (20, 2, 4, 16384),
-                                     (26000, 3, 3, 128), (40000, 4, 6, 128), (3000, 8, 600, 128)])
+                                     (26000, 3, 3, 128), (40000, 4, 6, 128), (3000, 8, 600, 128),
+                                     (9, 70, 128, 256), (6, 300, 1024, 128)])
 def test_small(T, k, G, K):
     x = S.activations(T, K, S.rng_for(1000 + T, K))
     check_against_oracle(x, routing(T, k, G, 1001 + T, drop_every=7), G)
@@ -72,6 +77,22 @@ def test_repeated_expert_choices_and_zero_tokens():
     x[3] = 0
     ids = np.tile(np.array([[1, 1, 0]], np.int32), (40, 1))
     check_against_oracle(x, ids, 2)
+
+
+def test_row_map_without_codes():
+    """K == 0: only the offsets and the slot -> row map are produced."""
+    import fp8_fine_grained_online_amd as F
+    import torch
+    from oracle import moe
+    T, k, G = 1000, 8, 32
+    ids = routing(T, k, G, 1005, drop_every=5)
+    x = torch.empty((T, 0), dtype=torch.bfloat16, device="cuda")
+    _, _, off, rows = F.fp8q_moe_dispatch_1x128(x, to_dev(ids), G)
+    torch.cuda.synchronize()
+    # the oracle's row assignment on zero tokens of one tile (rows do not depend on K)
+    _, _, off_o, rows_o, _ = moe.dispatch_1x128(np.zeros((T, 128), np.uint16), ids, G)
+    assert np.array_equal(off.cpu().numpy(), off_o)
+    assert np.array_equal(rows.cpu().numpy(), rows_o)
 
 
 def test_no_tokens_writes_zero_offsets():
