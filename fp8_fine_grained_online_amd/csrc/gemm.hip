@@ -151,16 +151,42 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, uint8_t* __restrict
   const float* sbmat = p.sb;
   if constexpr (kGrouped) {
     // tiles are numbered expert by expert (ceil(rows_e / BM) x n_tiles_n each),
-    // banded within an expert
-    int e = 0, before = 0, lo = 0, hi = 0, te = 0;
-    for (; e < p.G; ++e) {
-      lo = min(max(p.m_offsets[e], 0), p.M);
-      hi = min(max(p.m_offsets[e + 1], lo), p.M);
-      te = (hi - lo + BM - 1) / BM;
-      if (tile < before + te * n_tiles_n) break;
-      before += te * n_tiles_n;
+    // banded within an expert. The tile's expert: one expert per lane, 64 per
+    // round, an inclusive prefix of their tile counts across the lanes, and
+    // the first lane whose prefix passes the tile; its values are read back
+    // with readlane, so they stay scalar (lane shuffles would make them vector
+    // values, and every buffer descriptor built from them a loop). A loop over
+    // the experts one by one cost 2.8% with 70 experts (1969.5 against
+    // 2026.9 us, same results bit for bit; unchanged with 32).
+    int e = -1, before = 0, lo = 0, hi = 0, te = 0;
+    for (int e0 = 0; e0 < p.G; e0 += 64) {
+      const int ee = e0 + lane;
+      int l_lo = 0, l_hi = 0, l_te = 0;
+      if (ee < p.G) {
+        l_lo = min(max(p.m_offsets[ee], 0), p.M);
+        l_hi = min(max(p.m_offsets[ee + 1], l_lo), p.M);
+        l_te = (l_hi - l_lo + BM - 1) / BM;
+      }
+      const int cnt = l_te * n_tiles_n;
+      int incl = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+      }
+      const uint64_t hit = __ballot(ee < p.G && tile < before + incl);
+      if (hit) {
+        const int L = __builtin_ctzll(hit);
+        e = e0 + L;
+        lo = __builtin_amdgcn_readlane(l_lo, L);
+        hi = __builtin_amdgcn_readlane(l_hi, L);
+        te = __builtin_amdgcn_readlane(l_te, L);
+        before += __builtin_amdgcn_readlane(incl - cnt, L);
+        break;
+      }
+      before += __builtin_amdgcn_readlane(incl, 63);
     }
-    if (e == p.G) return;  // beyond the last real tile (grid is an upper bound)
+    if (e < 0) return;  // beyond the last real tile (grid is an upper bound)
     int tm;
     band_tile<kBandGrouped>(tile - before, te, n_tiles_n, tm, tile_n);
     m0 = lo + tm * BM;
